@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the DHSA sparse prefill path on one MI355X.
+
+One step = one attention layer's whole hot path on the Llama-3.1-8B layer
+shape at 128K context: dhsa_build_mask (pool + chunk scores + causal top-k)
+then dhsa_sparse_prefill (block-sparse causal attention), inputs resident in
+HBM.  Prints ONE JSON line:
+  value        kept-tile TFLOP/s over the whole layer (mask + attention)
+  ms_per_step  ms per layer
+  roofline     the attention kernel against the bf16 MFMA peak
+  cpu_baseline the CPU oracle on a bounded sample of the same layer
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+ATTN_SOURCES = ["long_context_prefill_segmented_amd/csrc/attn.hip"]
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_llama31_8b_128k_pmc.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kept_tile_flops(offsets, row_ptr, col_idx, hq, d=128):
+    """Algorithmic FLOPs of the kept tiles: 4*d per visible (query, key) pair;
+    the diagonal chunk counts its causal half n(n+1)/2."""
+    total = 0
+    r = 0
+    for o in offsets:
+        n = np.diff(np.asarray(o, dtype=np.int64))
+        C = n.size
+        for _h in range(hq):
+            for i in range(C):
+                cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+                r += 1
+                off = cols[cols < i]
+                total += int(n[i]) * int(n[off].sum())
+                if np.any(cols == i):
+                    total += int(n[i]) * (int(n[i]) + 1) // 2
+    return 4 * d * total
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(x, rows_gpu_unused, hq, hkv, budget_rows=24, seed=0):
+    """The oracle, untuned, on a bounded sample of the layer: full-layer mask
+    construction plus attention for a seeded sample of (head, query chunk)
+    rows, scaled to kept-tile TFLOP/s."""
+    from oracle import dhsa_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    b = 0
+    t0 = time.perf_counter()
+    q = orc.widen_bf16(x.q[b])
+    k = orc.widen_bf16(x.k[b])
+    _, _, _, _, rows = orc.build_mask(q, k, x.offsets[b], x.topk)
+    t_mask = time.perf_counter() - t0
+    v = orc.widen_bf16(x.v[b])
+    rng = np.random.default_rng(seed)
+    o = np.asarray(x.offsets[b], dtype=np.int64)
+    C = o.size - 1
+    n = np.diff(o)
+    G = hq // hkv
+    picks = [(int(rng.integers(0, hq)), int(rng.integers(0, C))) for _ in range(budget_rows)]
+    flops = 0
+    t1 = time.perf_counter()
+    for (h, i) in picks:
+        orc.chunk_attention(q, k, v, o, rows[h][i], i, h, h // G, 1.0 / math.sqrt(128))
+        cols = np.asarray(rows[h][i])
+        flops += 4 * 128 * (int(n[i]) * int(n[cols[cols < i]].sum()) + int(n[i]) * (int(n[i]) + 1) // 2)
+    t_att = time.perf_counter() - t1
+    rows_total = hq * C * x.workload.batch
+    frac = budget_rows / rows_total
+    t_layer_share = t_att + t_mask * frac
+    return {
+        "value": flops / t_layer_share / 1e12,
+        "unit": "TFLOP/s (kept tiles)",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"oracle (NumPy float64) mask construction of the whole layer ({t_mask:.1f} s, "
+                   f"prorated by {frac:.2e}) + attention of {budget_rows} seeded (head, query "
+                   f"chunk) rows ({t_att:.1f} s, {flops / 1e9:.1f} GFLOP kept)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama31_8b_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
+              "single-GPU by design", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_prefill_segmented_amd import dhsa, synth
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name} (seed {w.seed})")
+    x = synth.generate(w)
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    offs = dhsa.ChunkOffsets.from_list(x.offsets, w.seq_len, device=dev)
+    q = dhsa.bf16_from_bits(x.q, dev)
+    k = dhsa.bf16_from_bits(x.k, dev)
+    v = dhsa.bf16_from_bits(x.v, dev)
+    mb = dhsa.MaskBuilder(offs, hq, hkv, x.topk, device=dev)
+    pf = dhsa.Prefill(offs, hq, hkv, device=dev)
+    stream = torch.cuda.current_stream()
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        bb = torch.empty_like(a)
+        bb.copy_(a)
+        torch.cuda.synchronize()
+        del a, bb
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        csr = mb(q, k)
+        pf(q, k, v, csr)
+    torch.cuda.synchronize()
+    csr = mb(q, k)
+    torch.cuda.synchronize()
+    rp = csr.row_ptr.cpu().numpy()
+    ci = csr.col_idx.cpu().numpy()[:csr.nnz]
+    flops = kept_tile_flops(x.offsets, rp, ci, hq)
+    total_pairs = sum(len(o) - 1 for o in x.offsets)
+    mask_bytes = 2 * w.batch * w.seq_len * (hq + hkv) * 128 + 4 * (rp.size + ci.size)
+
+    log(f"[bench] timing {args.steps} steps")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        csr = mb(q, k)
+        ev[s][1].record(stream)
+        pf(q, k, v, csr)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mask_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    attn_ms = [b.elapsed_time(c) for _, b, c in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    attn_avg = statistics.mean(attn_ms)
+    mask_avg = statistics.mean(mask_ms)
+    log(f"[bench] mask {mask_avg:.3f} ms  attention {attn_avg:.3f} ms  wall/step {ms_per_step:.3f} ms")
+
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        try:
+            pm = json.load(open(PMC_FILE))
+            if pm.get("source_hash") == source_hash(ATTN_SOURCES) and pm.get("workload") == w.name:
+                traffic = pm.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a bounded sample)")
+        cpu = cpu_baseline(x, None, hq, hkv)
+
+    line = {
+        "metric": "sparse prefill ms/layer + kept-tile TFLOP/s, Llama-3.1-8B layer shape @128K",
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s (kept tiles, whole layer incl. mask construction)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; chunk offsets and values drawn per the workload recipe)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
+                   "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128, "topk": x.topk,
+                   "num_chunks": [len(o) - 1 for o in x.offsets], "nnz": int(ci.size)},
+        "mask_ms": mask_avg,
+        "attention_ms": attn_avg,
+        "mask_GBps": mask_bytes / (mask_avg * 1e-3) / 1e9,
+        "mask_hbm_frac": mask_bytes / (mask_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "kept_tile_TFLOP": flops / 1e12,
+        "chunk_pairs": total_pairs,
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * dhsa.h -- C ABI of the DHSA (Dynamic Hierarchical Sparse Attention) prefill
+ * path for one causal attention layer on an AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the prefill of one decoder attention layer: BF16, causal,
+ * forward only, head dimension 128, grouped-query attention (DHSA README,
+ * "Installation": the sparse kernel is BF16, causal, forward-only and needs
+ * head dimension 128; "Overview": DHSA handles prompt prefill only).  The
+ * method sits between the query/key projections and the attention backend
+ * (gist.science Technical Summary, "Key Contributions": drop-in module).
+ *
+ * Two calls make the path:
+ *   dhsa_build_mask     q, k, chunk offsets, top-k  ->  CSR block list
+ *   dhsa_sparse_prefill q, k, v, CSR                ->  out (and optional LSE)
+ * and three stage calls expose its steps one by one (pool, chunk scores,
+ * top-k) for stage-wise checking.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tensors are dense, contiguous, row-major and live in device memory:
+ *   q    bf16 [B][L][Hq][128]      k, v  bf16 [B][L][Hkv][128]
+ *   out  bf16 [B][L][Hq][128]      lse   f32  [B][Hq][L]   (natural log)
+ * bf16 values are passed as raw 16-bit patterns (uint16) through void*.
+ * Query head h reads KV head h / (Hq / Hkv).
+ *
+ * Chunks.  Sequence b is cut into C_b chunks by offsets o_0 = 0 < o_1 < ... <
+ * o_{C_b} = L (chunk c holds tokens [o_c, o_{c+1})).  The offsets of all
+ * sequences are concatenated, C_b + 1 entries per sequence.  Every call that
+ * needs them takes BOTH a host copy (chunk_offsets, used to validate and to
+ * size launches) and a device copy with the same values (chunk_offsets_dev,
+ * read by the kernels); the library never copies between them.
+ *
+ * Rows.  A CSR row is one (sequence b, query head h, query chunk i), numbered
+ * r = Hq * cbase_b + h * C_b + i with cbase_b = C_0 + ... + C_{b-1}.
+ * row_ptr has R + 1 entries (R = Hq * sum_b C_b), col_idx holds chunk
+ * indices local to the sequence, ascending within a row.
+ *
+ * Ownership.  The caller allocates and frees every buffer (inputs, outputs,
+ * workspaces).  The library allocates nothing and keeps no state besides a
+ * thread-local error string.
+ *
+ * Asynchrony.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the calls never synchronise.  Host-side inputs may be released
+ * as soon as a call returns.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued;
+ * on an error the call returns a negative status, enqueues nothing and
+ * writes nothing.  DHSA_ERR_HIP reports a failed launch.  dhsa_last_error()
+ * returns the calling thread's last message.  No C++ exception crosses the
+ * ABI.
+ *
+ * Limits: 1 <= B <= DHSA_MAX_BATCH, head_dim == 128, Hq % Hkv == 0,
+ * 1 <= C_b <= DHSA_MAX_CHUNKS for calls that select (the top-k keeps one
+ * candidate set of a row in registers).
+ */
+#ifndef DHSA_H
+#define DHSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DHSA_HEAD_DIM 128
+#define DHSA_MAX_BATCH 64
+#define DHSA_MAX_CHUNKS 2048
+
+typedef enum dhsa_status {
+  DHSA_OK = 0,
+  DHSA_ERR_NULL_POINTER = -1,   /* a required pointer is NULL               */
+  DHSA_ERR_SHAPE = -2,          /* batch/heads/head_dim/seq_len not allowed */
+  DHSA_ERR_OFFSETS = -3,        /* offsets not 0 < ... < L, or C_b invalid  */
+  DHSA_ERR_TOPK = -4,           /* topk < 1                                 */
+  DHSA_ERR_CAPACITY = -5,       /* output or workspace buffer too small     */
+  DHSA_ERR_CSR = -6,            /* CSR size arguments inconsistent          */
+  DHSA_ERR_UNSUPPORTED = -7,    /* beyond a documented limit                */
+  DHSA_ERR_HIP = -8             /* a HIP launch failed                      */
+} dhsa_status;
+
+/* Status name, e.g. "DHSA_ERR_OFFSETS".  Never NULL. */
+const char* dhsa_status_string(int status);
+
+/* Last error message of the calling thread ("" if none).  Never NULL. */
+const char* dhsa_last_error(void);
+
+/* ABI version of this library (major * 100 + minor). */
+int dhsa_version(void);
+
+/* ------------------------------------------------------------------------
+ * Sizes (host only; no device access)
+ * ---------------------------------------------------------------------- */
+
+/* CSR sizes for a fixed row budget: row i of a sequence keeps min(topk, i+1)
+ * chunks, so R = Hq * sum_b C_b and nnz = Hq * sum_b sum_i min(topk, i+1).
+ * (DHSA README, "Predictor Checkpoints": static predictors use a fixed row
+ * budget.)  num_chunks: host [batch].  Outputs may not be NULL. */
+int dhsa_csr_size(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
+                  int32_t topk, int32_t* num_rows, int64_t* nnz);
+
+/* Bytes of device workspace dhsa_build_mask needs: pooled Q and K (fp32) and
+ * the chunk-score matrices (fp32), each 256-byte aligned. */
+int dhsa_mask_workspace_size(int32_t batch, const int32_t* num_chunks,
+                             int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, size_t* bytes);
+
+/* Bytes of device workspace dhsa_sparse_prefill needs (its query-tile list);
+ * depends on the chunk lengths, hence the host offsets. */
+int dhsa_prefill_workspace_size(int32_t batch, int32_t seq_len,
+                                const int32_t* num_chunks,
+                                const int32_t* chunk_offsets, size_t* bytes);
+
+/* ------------------------------------------------------------------------
+ * The two calls of the path
+ * ---------------------------------------------------------------------- */
+
+/* Mask construction: length-normalised pooling of Q and K per chunk, chunk
+ * scores, and a causal top-k per query chunk, written as CSR.
+ *   - pooling: qbar[b,h,c] = (sum of q over chunk c) / n_c * sqrt(n_c)
+ *     (OpenReview abstract "...for On-Device LLMs": the averaged embeddings
+ *     are scaled by the square root of the chunk size; gist.science
+ *     Technical Summary, "Robust Chunk Representation");
+ *   - scores: S[b,h,i,j] = qbar[b,h,i] . kbar[b,h/G,j] for j <= i, fp32,
+ *     no 1/sqrt(d) (Technical Summary, Methodology, Step 1);
+ *   - selection: row (b,h,i) keeps chunk i and the topk-1 earlier chunks
+ *     with the highest scores, ties to the lower index, -0 == +0; all of
+ *     0..i when i + 1 <= topk (Methodology, Step 2: causal selection; the
+ *     kept chunks expand to their tokens, which dhsa_sparse_prefill does).
+ * Inputs:  q, k (device bf16, see conventions), sizes, offsets (host and
+ *          device copies), topk >= 1.
+ * Outputs: row_ptr device int32 [R+1]; col_idx device int32 [col_capacity],
+ *          col_capacity >= nnz of dhsa_csr_size; scores_out (nullable)
+ *          device fp32, per sequence [Hq][C_b][C_b] concatenated, entries
+ *          with j > i are not written.
+ * workspace: device, >= dhsa_mask_workspace_size bytes, 256-byte aligned.
+ * Errors: NULL pointers, shapes, offsets, topk, capacity, C_b >
+ *         DHSA_MAX_CHUNKS. */
+int dhsa_build_mask(const void* q, const void* k,
+                    int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim,
+                    const int32_t* num_chunks, const int32_t* chunk_offsets,
+                    const int32_t* chunk_offsets_dev, int32_t topk,
+                    int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                    float* scores_out, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Block-sparse causal attention forward over the kept chunk tiles.
+ * For query token t of chunk i, head h: out = softmax(scale * q_t k_s^T) v_s
+ * over the tokens s of the kept chunks of row (b,h,i) with s <= t (token-
+ * causal inside the diagonal chunk), computed tile by tile with an online
+ * softmax so no score matrix is stored (gist.science Technical Summary,
+ * "Hardware-Agnostic Backends": tiled online-softmax backend; DHSA README,
+ * "Overview": block-sparse attention with variable-sized query and key
+ * blocks).  Accumulation is fp32; out is rounded to bf16.
+ * Inputs:  q, k, v device bf16; CSR row_ptr/col_idx (device, nnz entries)
+ *          from dhsa_build_mask or any source whose rows are strictly
+ *          ascending with entries in [0, i]; softmax_scale <= 0 selects
+ *          1/sqrt(128).
+ * Outputs: out device bf16 [B][L][Hq][128]; lse (nullable) device fp32
+ *          [B][Hq][L].  A query with no visible key gets out = 0 and
+ *          lse = -inf.
+ * workspace: device, >= dhsa_prefill_workspace_size bytes.
+ * The kernels bound-check CSR entries (entries outside [0, i] and row_ptr
+ * values outside [0, nnz] are ignored), so a malformed CSR gives wrong
+ * values but no out-of-bounds access. */
+int dhsa_sparse_prefill(const void* q, const void* k, const void* v,
+                        int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim,
+                        const int32_t* num_chunks, const int32_t* chunk_offsets,
+                        const int32_t* chunk_offsets_dev,
+                        const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                        float softmax_scale, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage calls (the steps of dhsa_build_mask one at a time)
+ * ---------------------------------------------------------------------- */
+
+/* Pooling of one tensor x (device bf16 [B][L][H][128]) into pooled (device
+ * fp32 [sum_b H*C_b][128], row H*cbase_b + h*C_b + c).  Citation as for the
+ * pooling step of dhsa_build_mask. */
+int dhsa_pool(const void* x, int32_t batch, int32_t seq_len, int32_t num_heads,
+              int32_t head_dim, const int32_t* num_chunks,
+              const int32_t* chunk_offsets, const int32_t* chunk_offsets_dev,
+              float* pooled, void* stream);
+
+/* Chunk scores from pooled Q (fp32 rows as dhsa_pool with H = Hq) and
+ * pooled K (H = Hkv) into scores (device fp32, per sequence [Hq][C_b][C_b]
+ * concatenated; j > i not written). */
+int dhsa_chunk_scores(const float* qbar, const float* kbar, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      const int32_t* num_chunks, float* scores, void* stream);
+
+/* Causal top-k of given fp32 chunk scores (layout of dhsa_chunk_scores) into
+ * CSR, with the selection rule of dhsa_build_mask.  NaN scores rank below
+ * every number. */
+int dhsa_topk_csr(const float* scores, int32_t batch, int32_t num_q_heads,
+                  const int32_t* num_chunks, int32_t topk, int32_t* row_ptr,
+                  int32_t* col_idx, int64_t col_capacity, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DHSA_H */

@@ -1,0 +1,381 @@
+// Host side of the C ABI: argument validation, sizes, launch planning.
+// Every check runs before any HIP call; on an error nothing is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "dhsa_internal.h"
+
+namespace dhsa {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DHSA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DHSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_batch_chunks(int32_t batch, const int32_t* num_chunks) {
+  if (num_chunks == nullptr) return fail(DHSA_ERR_NULL_POINTER, "num_chunks is NULL");
+  if (batch < 1 || batch > kMaxBatch)
+    return fail(DHSA_ERR_SHAPE, "batch %d outside [1, %d]", batch, kMaxBatch);
+  int64_t total = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (num_chunks[b] < 1)
+      return fail(DHSA_ERR_OFFSETS, "sequence %d has %d chunks", b, num_chunks[b]);
+    total += num_chunks[b];
+  }
+  if (total > INT32_MAX / 4) return fail(DHSA_ERR_UNSUPPORTED, "too many chunks (%lld)", (long long)total);
+  return DHSA_OK;
+}
+
+int check_heads(int32_t hq, int32_t hkv, int32_t head_dim) {
+  if (head_dim != kHeadDim) return fail(DHSA_ERR_SHAPE, "head_dim %d != %d", head_dim, kHeadDim);
+  if (hq < 1 || hkv < 1) return fail(DHSA_ERR_SHAPE, "head counts must be >= 1 (%d, %d)", hq, hkv);
+  if (hq % hkv) return fail(DHSA_ERR_SHAPE, "num_q_heads %d not a multiple of num_kv_heads %d", hq, hkv);
+  return DHSA_OK;
+}
+
+int check_offsets(int32_t batch, int32_t seq_len, const int32_t* num_chunks,
+                  const int32_t* offs) {
+  if (offs == nullptr) return fail(DHSA_ERR_NULL_POINTER, "chunk_offsets is NULL");
+  if (seq_len < 1) return fail(DHSA_ERR_SHAPE, "seq_len %d < 1", seq_len);
+  size_t o = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int C = num_chunks[b];
+    if (C > seq_len) return fail(DHSA_ERR_OFFSETS, "sequence %d: %d chunks > seq_len", b, C);
+    if (offs[o] != 0) return fail(DHSA_ERR_OFFSETS, "sequence %d: offsets must start at 0", b);
+    for (int c = 0; c < C; ++c) {
+      if (offs[o + c + 1] <= offs[o + c])
+        return fail(DHSA_ERR_OFFSETS, "sequence %d: offsets not strictly increasing at %d", b, c);
+    }
+    if (offs[o + C] != seq_len)
+      return fail(DHSA_ERR_OFFSETS, "sequence %d: offsets end at %d, not seq_len %d", b, offs[o + C],
+                  seq_len);
+    o += C + 1;
+  }
+  return DHSA_OK;
+}
+
+int64_t entries_per_head(int64_t C, int64_t k) {
+  return C <= k ? C * (C + 1) / 2 : k * (k + 1) / 2 + (C - k) * k;
+}
+
+void fill_table(SeqTable& st, int32_t batch, const int32_t* num_chunks, int32_t hq,
+                int32_t topk) {
+  memset(&st, 0, sizeof(st));
+  st.batch = batch;
+  int64_t cb = 0, sb = 0, nb = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t C = num_chunks[b];
+    st.num_chunks[b] = (int32_t)C;
+    st.cbase[b] = (int32_t)cb;
+    st.sbase[b] = sb;
+    st.nbase[b] = nb;
+    cb += C;
+    sb += (int64_t)hq * C * C;
+    if (topk > 0) nb += (int64_t)hq * entries_per_head(C, topk);
+  }
+}
+
+int64_t total_chunks(int32_t batch, const int32_t* num_chunks) {
+  int64_t t = 0;
+  for (int b = 0; b < batch; ++b) t += num_chunks[b];
+  return t;
+}
+
+int64_t score_elems(int32_t batch, const int32_t* num_chunks, int32_t hq) {
+  int64_t t = 0;
+  for (int b = 0; b < batch; ++b) t += (int64_t)hq * num_chunks[b] * num_chunks[b];
+  return t;
+}
+
+int64_t score_tiles(int32_t batch, const int32_t* num_chunks, int32_t hq) {
+  int64_t t = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t T = (num_chunks[b] + 31) / 32;
+    t += hq * T * (T + 1) / 2;
+  }
+  return t;
+}
+
+int64_t query_tiles(int32_t batch, const int32_t* num_chunks, const int32_t* offs,
+                    int32_t* tbase) {
+  int64_t t = 0;
+  size_t o = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (tbase) tbase[b] = (int32_t)t;
+    for (int c = 0; c < num_chunks[b]; ++c)
+      t += (offs[o + c + 1] - offs[o + c] + kBlockM - 1) / kBlockM;
+    o += num_chunks[b] + 1;
+  }
+  return t;
+}
+
+int max_chunks(int32_t batch, const int32_t* num_chunks) {
+  int m = 0;
+  for (int b = 0; b < batch; ++b) m = num_chunks[b] > m ? num_chunks[b] : m;
+  return m;
+}
+
+}  // namespace
+}  // namespace dhsa
+
+using namespace dhsa;
+
+extern "C" {
+
+const char* dhsa_status_string(int status) {
+  switch (status) {
+    case DHSA_OK: return "DHSA_OK";
+    case DHSA_ERR_NULL_POINTER: return "DHSA_ERR_NULL_POINTER";
+    case DHSA_ERR_SHAPE: return "DHSA_ERR_SHAPE";
+    case DHSA_ERR_OFFSETS: return "DHSA_ERR_OFFSETS";
+    case DHSA_ERR_TOPK: return "DHSA_ERR_TOPK";
+    case DHSA_ERR_CAPACITY: return "DHSA_ERR_CAPACITY";
+    case DHSA_ERR_CSR: return "DHSA_ERR_CSR";
+    case DHSA_ERR_UNSUPPORTED: return "DHSA_ERR_UNSUPPORTED";
+    case DHSA_ERR_HIP: return "DHSA_ERR_HIP";
+    default: return "DHSA_ERR_UNKNOWN";
+  }
+}
+
+const char* dhsa_last_error(void) { return g_err; }
+
+int dhsa_version(void) { return 100; }
+
+int dhsa_csr_size(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads, int32_t topk,
+                  int32_t* num_rows, int64_t* nnz) {
+  if (num_rows == nullptr || nnz == nullptr) return fail(DHSA_ERR_NULL_POINTER, "output pointer is NULL");
+  int s = check_batch_chunks(batch, num_chunks);
+  if (s) return s;
+  if (num_q_heads < 1) return fail(DHSA_ERR_SHAPE, "num_q_heads %d < 1", num_q_heads);
+  if (topk < 1) return fail(DHSA_ERR_TOPK, "topk %d < 1", topk);
+  int64_t R = 0, N = 0;
+  for (int b = 0; b < batch; ++b) {
+    R += (int64_t)num_q_heads * num_chunks[b];
+    N += (int64_t)num_q_heads * entries_per_head(num_chunks[b], topk);
+  }
+  if (R > INT32_MAX - 1 || N > INT32_MAX)
+    return fail(DHSA_ERR_UNSUPPORTED, "CSR too large for int32 indices");
+  *num_rows = (int32_t)R;
+  *nnz = N;
+  return ok();
+}
+
+int dhsa_mask_workspace_size(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, size_t* bytes) {
+  if (bytes == nullptr) return fail(DHSA_ERR_NULL_POINTER, "bytes is NULL");
+  int s = check_batch_chunks(batch, num_chunks);
+  if (s) return s;
+  s = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (s) return s;
+  const int64_t tc = total_chunks(batch, num_chunks);
+  size_t n = align_up((size_t)num_q_heads * tc * kHeadDim * sizeof(float));
+  n += align_up((size_t)num_kv_heads * tc * kHeadDim * sizeof(float));
+  n += align_up((size_t)score_elems(batch, num_chunks, num_q_heads) * sizeof(float));
+  *bytes = n;
+  return ok();
+}
+
+int dhsa_prefill_workspace_size(int32_t batch, int32_t seq_len, const int32_t* num_chunks,
+                                const int32_t* chunk_offsets, size_t* bytes) {
+  if (bytes == nullptr) return fail(DHSA_ERR_NULL_POINTER, "bytes is NULL");
+  int s = check_batch_chunks(batch, num_chunks);
+  if (s) return s;
+  s = check_offsets(batch, seq_len, num_chunks, chunk_offsets);
+  if (s) return s;
+  *bytes = align_up((size_t)query_tiles(batch, num_chunks, chunk_offsets, nullptr) * sizeof(int4));
+  return ok();
+}
+
+int dhsa_pool(const void* x, int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
+              const int32_t* num_chunks, const int32_t* chunk_offsets,
+              const int32_t* chunk_offsets_dev, float* pooled, void* stream) {
+  if (!x || !pooled || !chunk_offsets_dev) return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
+  int s = check_batch_chunks(batch, num_chunks);
+  if (s) return s;
+  s = check_heads(num_heads, 1, head_dim);
+  if (s) return s;
+  s = check_offsets(batch, seq_len, num_chunks, chunk_offsets);
+  if (s) return s;
+  SeqTable st;
+  fill_table(st, batch, num_chunks, num_heads, 0);
+  hipError_t e = launch_pool(static_cast<const uint16_t*>(x), pooled, num_heads, nullptr, nullptr, 0,
+                             (int32_t)total_chunks(batch, num_chunks), chunk_offsets_dev, st, seq_len,
+                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  return ok();
+}
+
+int dhsa_chunk_scores(const float* qbar, const float* kbar, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, const int32_t* num_chunks,
+                      float* scores, void* stream) {
+  if (!qbar || !kbar || !scores) return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
+  int s = check_batch_chunks(batch, num_chunks);
+  if (s) return s;
+  s = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (s) return s;
+  SeqTable st;
+  fill_table(st, batch, num_chunks, num_q_heads, 0);
+  const int64_t tiles = score_tiles(batch, num_chunks, num_q_heads);
+  if (tiles > INT32_MAX) return fail(DHSA_ERR_UNSUPPORTED, "too many score tiles");
+  hipError_t e = launch_scores(qbar, kbar, scores, num_q_heads, num_kv_heads, st, tiles,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "chunk score launch");
+  return ok();
+}
+
+int dhsa_topk_csr(const float* scores, int32_t batch, int32_t num_q_heads,
+                  const int32_t* num_chunks, int32_t topk, int32_t* row_ptr, int32_t* col_idx,
+                  int64_t col_capacity, void* stream) {
+  if (!scores || !row_ptr || !col_idx) return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
+  int32_t R;
+  int64_t nnz;
+  int s = dhsa_csr_size(batch, num_chunks, num_q_heads, topk, &R, &nnz);
+  if (s) return s;
+  if (max_chunks(batch, num_chunks) > kMaxChunks)
+    return fail(DHSA_ERR_UNSUPPORTED, "more than %d chunks in a sequence", kMaxChunks);
+  if (col_capacity < nnz)
+    return fail(DHSA_ERR_CAPACITY, "col_capacity %lld < nnz %lld", (long long)col_capacity,
+                (long long)nnz);
+  SeqTable st;
+  fill_table(st, batch, num_chunks, num_q_heads, topk);
+  hipError_t e = launch_topk(scores, st, num_q_heads, R, topk, max_chunks(batch, num_chunks),
+                             row_ptr, col_idx, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+int dhsa_build_mask(const void* q, const void* k, int32_t batch, int32_t seq_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    const int32_t* num_chunks, const int32_t* chunk_offsets,
+                    const int32_t* chunk_offsets_dev, int32_t topk, int32_t* row_ptr,
+                    int32_t* col_idx, int64_t col_capacity, float* scores_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!q || !k || !chunk_offsets_dev || !row_ptr || !col_idx || !workspace)
+    return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
+  int s = check_batch_chunks(batch, num_chunks);
+  if (s) return s;
+  s = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (s) return s;
+  s = check_offsets(batch, seq_len, num_chunks, chunk_offsets);
+  if (s) return s;
+  int32_t R;
+  int64_t nnz;
+  s = dhsa_csr_size(batch, num_chunks, num_q_heads, topk, &R, &nnz);
+  if (s) return s;
+  if (max_chunks(batch, num_chunks) > kMaxChunks)
+    return fail(DHSA_ERR_UNSUPPORTED, "more than %d chunks in a sequence", kMaxChunks);
+  if (col_capacity < nnz)
+    return fail(DHSA_ERR_CAPACITY, "col_capacity %lld < nnz %lld", (long long)col_capacity,
+                (long long)nnz);
+  size_t need;
+  s = dhsa_mask_workspace_size(batch, num_chunks, num_q_heads, num_kv_heads, head_dim, &need);
+  if (s) return s;
+  if (workspace_bytes < need)
+    return fail(DHSA_ERR_CAPACITY, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DHSA_ERR_CAPACITY, "workspace not %zu-byte aligned", kAlign);
+
+  const int64_t tc = total_chunks(batch, num_chunks);
+  char* ws = static_cast<char*>(workspace);
+  float* qbar = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)num_q_heads * tc * kHeadDim * sizeof(float));
+  float* kbar = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)num_kv_heads * tc * kHeadDim * sizeof(float));
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
+
+  SeqTable st;
+  fill_table(st, batch, num_chunks, num_q_heads, topk);
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_pool(static_cast<const uint16_t*>(q), qbar, num_q_heads,
+                             static_cast<const uint16_t*>(k), kbar, num_kv_heads, (int32_t)tc,
+                             chunk_offsets_dev, st, seq_len, strm);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  e = launch_scores(qbar, kbar, scores, num_q_heads, num_kv_heads, st,
+                    score_tiles(batch, num_chunks, num_q_heads), strm);
+  if (e != hipSuccess) return hip_fail(e, "chunk score launch");
+  e = launch_topk(scores, st, num_q_heads, R, topk, max_chunks(batch, num_chunks), row_ptr,
+                  col_idx, strm);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t batch,
+                        int32_t seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, const int32_t* num_chunks, const int32_t* chunk_offsets,
+                        const int32_t* chunk_offsets_dev, const int32_t* row_ptr,
+                        const int32_t* col_idx, int64_t nnz, float softmax_scale, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !chunk_offsets_dev || !row_ptr || !out || !workspace)
+    return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
+  if (nnz > 0 && !col_idx) return fail(DHSA_ERR_NULL_POINTER, "col_idx is NULL");
+  if (nnz < 0 || nnz > INT32_MAX) return fail(DHSA_ERR_CSR, "nnz %lld out of range", (long long)nnz);
+  int s = check_batch_chunks(batch, num_chunks);
+  if (s) return s;
+  s = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (s) return s;
+  s = check_offsets(batch, seq_len, num_chunks, chunk_offsets);
+  if (s) return s;
+  if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale))
+    return fail(DHSA_ERR_SHAPE, "softmax_scale is not finite");
+  const int32_t ntiles_max = INT32_MAX / num_q_heads;
+  int32_t tbase[kMaxBatch];
+  const int64_t ntiles = query_tiles(batch, num_chunks, chunk_offsets, tbase);
+  if (ntiles > ntiles_max) return fail(DHSA_ERR_UNSUPPORTED, "too many query tiles");
+  const size_t need = align_up((size_t)ntiles * sizeof(int4));
+  if (workspace_bytes < need)
+    return fail(DHSA_ERR_CAPACITY, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DHSA_ERR_CAPACITY, "workspace not %zu-byte aligned", kAlign);
+
+  SeqTable st;
+  fill_table(st, batch, num_chunks, num_q_heads, 0);
+  for (int b = 0; b < batch; ++b) st.tbase[b] = tbase[b];
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  int4* tiles = static_cast<int4*>(workspace);
+  hipError_t e = launch_plan_tiles(chunk_offsets_dev, st, tiles, strm);
+  if (e != hipSuccess) return hip_fail(e, "tile plan launch");
+
+  AttnParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.tiles = tiles;
+  p.offs = chunk_offsets_dev;
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
+  p.nnz = nnz;
+  p.num_tiles = (int32_t)ntiles;
+  p.seq_len = seq_len;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  e = launch_attention(p, st, strm);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+}  // extern "C"

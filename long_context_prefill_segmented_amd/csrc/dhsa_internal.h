@@ -1,0 +1,79 @@
+// Internal declarations shared by the host entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dhsa.h"
+
+namespace dhsa {
+
+constexpr int kHeadDim = DHSA_HEAD_DIM;
+constexpr int kMaxBatch = DHSA_MAX_BATCH;
+constexpr int kMaxChunks = DHSA_MAX_CHUNKS;
+
+// Attention tiling: a workgroup owns kBlockM query rows of one query chunk
+// and one query head (4 waves x 32 rows) and streams the gathered kept keys
+// kBlockN at a time.
+constexpr int kBlockM = 128;
+constexpr int kBlockN = 64;
+
+// Per-sequence bookkeeping passed by value in kernel arguments (host
+// computed, so no upload is needed).
+struct SeqTable {
+  int32_t batch;
+  int32_t num_chunks[kMaxBatch];
+  int32_t cbase[kMaxBatch];    // sum of C over earlier sequences
+  int32_t tbase[kMaxBatch];    // first query tile of the sequence
+  int64_t sbase[kMaxBatch];    // first score element of the sequence
+  int64_t nbase[kMaxBatch];    // first CSR entry of the sequence
+};
+
+// Finds the sequence that owns global index x given per-sequence starts
+// (starts[0] == 0, nondecreasing).
+template <typename T>
+__device__ __forceinline__ int find_seq(const T* starts, int batch, T x) {
+  int b = 0;
+  while (b + 1 < batch && starts[b + 1] <= x) ++b;
+  return b;
+}
+
+// kernels' launchers (each returns hipGetLastError() of its launch)
+hipError_t launch_pool(const uint16_t* x0, float* out0, int32_t h0,
+                       const uint16_t* x1, float* out1, int32_t h1,
+                       int32_t total_chunks, const int32_t* offs_dev,
+                       const SeqTable& st, int32_t seq_len, hipStream_t stream);
+
+hipError_t launch_scores(const float* qbar, const float* kbar, float* scores,
+                         int32_t hq, int32_t hkv, const SeqTable& st,
+                         int64_t total_tiles, hipStream_t stream);
+
+hipError_t launch_topk(const float* scores, const SeqTable& st, int32_t hq,
+                       int32_t total_rows, int32_t topk, int32_t max_chunks,
+                       int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
+
+hipError_t launch_plan_tiles(const int32_t* offs_dev, const SeqTable& st,
+                             int4* tiles, hipStream_t stream);
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int4* tiles;
+  const int32_t* offs;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t nnz;
+  int32_t num_tiles;
+  int32_t seq_len;
+  int32_t hq;
+  int32_t hkv;
+  float scale_log2;
+};
+
+hipError_t launch_attention(const AttnParams& p, const SeqTable& st,
+                            hipStream_t stream);
+
+}  // namespace dhsa

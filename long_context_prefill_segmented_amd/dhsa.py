@@ -1,0 +1,298 @@
+"""Thin Python binding over libdhsa.so (argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers and sizes, allocates outputs and
+workspaces with torch (device memory and streams are all torch is used for),
+and raises on a non-zero status.  There is no fallback: importing it raises
+if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+# torch ships its own HIP runtime under the same soname as the system one
+# (libamdhip64.so.7); loading torch first makes libdhsa.so bind to that
+# already-loaded runtime, so the process holds ONE HIP runtime and torch's
+# device memory and streams are valid in the library's calls.
+import torch  # noqa: E402,F401  (must precede the CDLL below)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdhsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m long_context_prefill_segmented_amd.build_lib`")
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+_psz = ctypes.POINTER(ctypes.c_size_t)
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_SIGNATURES = {
+    "dhsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dhsa_last_error": (ctypes.c_char_p, []),
+    "dhsa_version": (ctypes.c_int, []),
+    "dhsa_csr_size": (ctypes.c_int, [_i32, _vp, _i32, _i32, _pi32, _pi64]),
+    "dhsa_mask_workspace_size": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _psz]),
+    "dhsa_prefill_workspace_size": (ctypes.c_int, [_i32, _i32, _vp, _vp, _psz]),
+    "dhsa_build_mask": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                       _i32, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "dhsa_sparse_prefill": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
+                                           _vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp, _vp, _sz,
+                                           _vp]),
+    "dhsa_pool": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "dhsa_chunk_scores": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "dhsa_topk_csr": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _i64, _vp]),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGNATURES)
+HEAD_DIM = 128
+ALIGN = 256
+
+
+class DhsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{lib.dhsa_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise DhsaError(status, lib.dhsa_last_error().decode())
+
+
+def _np_ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+# --------------------------------------------------------------------------
+# torch side: device memory and streams
+# --------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dptr(t) -> int:
+    return t.data_ptr()
+
+
+@dataclasses.dataclass
+class ChunkOffsets:
+    """Concatenated chunk offsets: host copy (validation, launch sizes) and a
+    device copy with the same values (read by the kernels)."""
+
+    host: np.ndarray          # int32 [sum_b (C_b + 1)]
+    num_chunks: np.ndarray    # int32 [B]
+    seq_len: int
+    device: object            # torch int32 tensor, same values
+
+    @classmethod
+    def from_list(cls, offsets: Sequence[np.ndarray], seq_len: int, device="cuda"):
+        torch = _torch()
+        host = np.ascontiguousarray(np.concatenate([np.asarray(o) for o in offsets]).astype(np.int32))
+        nc = np.ascontiguousarray(np.array([len(o) - 1 for o in offsets], dtype=np.int32))
+        dev = torch.from_numpy(host.copy()).to(device)
+        return cls(host, nc, int(seq_len), dev)
+
+    @property
+    def batch(self) -> int:
+        return int(self.num_chunks.size)
+
+
+@dataclasses.dataclass
+class CSR:
+    row_ptr: object   # torch int32 [R + 1]
+    col_idx: object   # torch int32 [nnz]
+    nnz: int
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.row_ptr.numel()) - 1
+
+
+def csr_size(offsets: ChunkOffsets, num_q_heads: int, topk: int):
+    R = _i32()
+    nnz = _i64()
+    check(lib.dhsa_csr_size(offsets.batch, _np_ptr(offsets.num_chunks), num_q_heads, topk,
+                            ctypes.byref(R), ctypes.byref(nnz)))
+    return R.value, nnz.value
+
+
+def mask_workspace_size(offsets: ChunkOffsets, hq: int, hkv: int) -> int:
+    n = _sz()
+    check(lib.dhsa_mask_workspace_size(offsets.batch, _np_ptr(offsets.num_chunks), hq, hkv,
+                                       HEAD_DIM, ctypes.byref(n)))
+    return n.value
+
+
+def prefill_workspace_size(offsets: ChunkOffsets) -> int:
+    n = _sz()
+    check(lib.dhsa_prefill_workspace_size(offsets.batch, offsets.seq_len,
+                                          _np_ptr(offsets.num_chunks), _np_ptr(offsets.host),
+                                          ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(nbytes, ALIGN), dtype=torch.uint8, device=device)
+
+
+def _check_qkv(q, k, v=None):
+    torch = _torch()
+    for t in (q, k) + ((v,) if v is not None else ()):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda or t.dim() != 4:
+            raise ValueError("q/k/v must be contiguous CUDA bfloat16 [B, L, H, 128] tensors")
+    if k.shape[:2] != q.shape[:2] or (v is not None and v.shape != k.shape):
+        raise ValueError("q, k, v shapes disagree")
+
+
+def scores_numel(offsets: ChunkOffsets, num_q_heads: int) -> int:
+    return int(sum(num_q_heads * int(c) * int(c) for c in offsets.num_chunks))
+
+
+class MaskBuilder:
+    """Preallocated buffers for repeated dhsa_build_mask calls on one shape."""
+
+    def __init__(self, offsets: ChunkOffsets, hq: int, hkv: int, topk: int, device="cuda",
+                 keep_scores: bool = False):
+        torch = _torch()
+        self.offsets, self.hq, self.hkv, self.topk = offsets, hq, hkv, topk
+        R, nnz = csr_size(offsets, hq, topk)
+        self.csr = CSR(torch.empty(R + 1, dtype=torch.int32, device=device),
+                       torch.empty(max(nnz, 1), dtype=torch.int32, device=device), nnz)
+        self.ws = _workspace(mask_workspace_size(offsets, hq, hkv), device)
+        self.scores = (torch.empty(scores_numel(offsets, hq), dtype=torch.float32, device=device)
+                       if keep_scores else None)
+
+    def __call__(self, q, k, stream=None) -> CSR:
+        o = self.offsets
+        check(lib.dhsa_build_mask(
+            _dptr(q), _dptr(k), o.batch, o.seq_len, self.hq, self.hkv, HEAD_DIM,
+            _np_ptr(o.num_chunks), _np_ptr(o.host), _dptr(o.device), self.topk,
+            _dptr(self.csr.row_ptr), _dptr(self.csr.col_idx), self.csr.col_idx.numel(),
+            _dptr(self.scores) if self.scores is not None else None,
+            _dptr(self.ws), self.ws.numel(), _stream_ptr(stream)))
+        return self.csr
+
+
+def build_mask(q, k, offsets: ChunkOffsets, topk: int, return_scores: bool = False,
+               stream=None):
+    """dhsa_build_mask: pooled chunk scores -> causal top-k CSR block list."""
+    _check_qkv(q, k)
+    B, L, hq, _ = q.shape
+    hkv = k.shape[2]
+    mb = MaskBuilder(offsets, hq, hkv, topk, device=q.device, keep_scores=return_scores)
+    csr = mb(q, k, stream)
+    return (csr, mb.scores) if return_scores else csr
+
+
+class Prefill:
+    """Preallocated buffers for repeated dhsa_sparse_prefill calls on one shape."""
+
+    def __init__(self, offsets: ChunkOffsets, hq: int, hkv: int, device="cuda",
+                 with_lse: bool = False, softmax_scale: float = 0.0):
+        torch = _torch()
+        self.offsets, self.hq, self.hkv = offsets, hq, hkv
+        self.scale = float(softmax_scale)
+        B, L = offsets.batch, offsets.seq_len
+        self.out = torch.empty((B, L, hq, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((B, hq, L), dtype=torch.float32, device=device) if with_lse else None
+        self.ws = _workspace(prefill_workspace_size(offsets), device)
+
+    def __call__(self, q, k, v, csr: CSR, stream=None):
+        o = self.offsets
+        check(lib.dhsa_sparse_prefill(
+            _dptr(q), _dptr(k), _dptr(v), o.batch, o.seq_len, self.hq, self.hkv, HEAD_DIM,
+            _np_ptr(o.num_chunks), _np_ptr(o.host), _dptr(o.device), _dptr(csr.row_ptr),
+            _dptr(csr.col_idx), csr.nnz, self.scale, _dptr(self.out),
+            _dptr(self.lse) if self.lse is not None else None,
+            _dptr(self.ws), self.ws.numel(), _stream_ptr(stream)))
+        return (self.out, self.lse) if self.lse is not None else self.out
+
+
+def sparse_prefill(q, k, v, offsets: ChunkOffsets, csr: CSR, softmax_scale: float = 0.0,
+                   return_lse: bool = False, stream=None):
+    """dhsa_sparse_prefill: block-sparse causal attention over the kept tiles."""
+    _check_qkv(q, k, v)
+    pf = Prefill(offsets, q.shape[2], k.shape[2], device=q.device, with_lse=return_lse,
+                 softmax_scale=softmax_scale)
+    return pf(q, k, v, csr, stream)
+
+
+def pool(x, offsets: ChunkOffsets, stream=None):
+    """dhsa_pool: fp32 [sum_b H*C_b, 128] pooled chunk representations."""
+    torch = _torch()
+    _check_qkv(x, x)
+    B, L, H, _ = x.shape
+    out = torch.empty((H * int(offsets.num_chunks.sum()), HEAD_DIM), dtype=torch.float32,
+                      device=x.device)
+    check(lib.dhsa_pool(_dptr(x), B, L, H, HEAD_DIM, _np_ptr(offsets.num_chunks),
+                        _np_ptr(offsets.host), _dptr(offsets.device), _dptr(out),
+                        _stream_ptr(stream)))
+    return out
+
+
+def chunk_scores(qbar, kbar, offsets: ChunkOffsets, hq: int, hkv: int, stream=None):
+    """dhsa_chunk_scores: fp32 per sequence [Hq, C_b, C_b] (j > i untouched: NaN here)."""
+    torch = _torch()
+    out = torch.full((scores_numel(offsets, hq),), float("nan"), dtype=torch.float32,
+                     device=qbar.device)
+    check(lib.dhsa_chunk_scores(_dptr(qbar), _dptr(kbar), offsets.batch, hq, hkv, HEAD_DIM,
+                                _np_ptr(offsets.num_chunks), _dptr(out), _stream_ptr(stream)))
+    return out
+
+
+def topk_csr(scores, offsets: ChunkOffsets, hq: int, topk: int, stream=None) -> CSR:
+    """dhsa_topk_csr: CSR from given fp32 chunk scores."""
+    torch = _torch()
+    if scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise ValueError("scores must be contiguous float32")
+    R, nnz = csr_size(offsets, hq, topk)
+    csr = CSR(torch.empty(R + 1, dtype=torch.int32, device=scores.device),
+              torch.empty(max(nnz, 1), dtype=torch.int32, device=scores.device), nnz)
+    check(lib.dhsa_topk_csr(_dptr(scores), offsets.batch, hq, _np_ptr(offsets.num_chunks), topk,
+                            _dptr(csr.row_ptr), _dptr(csr.col_idx), csr.col_idx.numel(),
+                            _stream_ptr(stream)))
+    return csr
+
+
+def csr_from_host(row_ptr: np.ndarray, col_idx: np.ndarray, device="cuda") -> CSR:
+    """Uploads a CSR built elsewhere (e.g. a reference mask) for dhsa_sparse_prefill."""
+    torch = _torch()
+    rp = torch.from_numpy(np.ascontiguousarray(row_ptr, dtype=np.int32)).to(device)
+    ci = torch.from_numpy(np.ascontiguousarray(col_idx, dtype=np.int32))
+    nnz = int(ci.numel())
+    if nnz == 0:
+        ci = torch.zeros(1, dtype=torch.int32)
+    return CSR(rp, ci.to(device), nnz)
+
+
+def bf16_from_bits(bits: np.ndarray, device="cuda"):
+    """uint16 bf16 bit patterns -> CUDA bfloat16 tensor (same bits)."""
+    torch = _torch()
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)

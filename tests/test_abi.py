@@ -1,0 +1,170 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+sizes CSR/workspaces, and rejects every invalid argument before touching the
+device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dhsa.h")
+
+dhsa = pytest.importorskip("long_context_prefill_segmented_amd.dhsa",
+                           reason="libdhsa.so not built")
+lib = dhsa.lib
+
+OK, ENULL, ESHAPE, EOFF, ETOPK, ECAP, ECSR, EUNSUP, EHIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+# error-path calls pass stand-in device addresses; they must be rejected on
+# the host, and they run only where no GPU is visible
+cpu_only = pytest.mark.skipif(_gpu_visible(), reason="error-path checks run on the CPU host")
+
+
+def test_every_declared_function_is_exported():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(dhsa_\w+)\s*\(", text, re.M))
+    assert len(declared) >= 11
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(dhsa.EXPORTED)
+
+
+def test_status_strings_and_version():
+    assert lib.dhsa_status_string(0) == b"DHSA_OK"
+    assert lib.dhsa_status_string(EOFF) == b"DHSA_ERR_OFFSETS"
+    assert lib.dhsa_status_string(12345) == b"DHSA_ERR_UNKNOWN"
+    assert lib.dhsa_version() >= 100
+
+
+def _arr(x, dt=np.int32):
+    return np.ascontiguousarray(np.asarray(x, dtype=dt))
+
+
+def _csr_size(nc, hq, k):
+    R = ctypes.c_int32()
+    N = ctypes.c_int64()
+    nc = _arr(nc)
+    s = lib.dhsa_csr_size(nc.size, nc.ctypes.data, hq, k, ctypes.byref(R), ctypes.byref(N))
+    return s, R.value, N.value
+
+
+def test_csr_size_closed_form():
+    for nc, hq, k in (([26], 2, 4), ([438], 32, 11), ([441, 564], 32, 16), ([5, 1, 9], 3, 100)):
+        s, R, N = _csr_size(nc, hq, k)
+        assert s == OK
+        assert R == hq * sum(nc)
+        assert N == hq * sum(sum(min(k, i + 1) for i in range(c)) for c in nc)
+
+
+def test_csr_size_errors():
+    assert _csr_size([10], 2, 0)[0] == ETOPK
+    assert _csr_size([0], 2, 3)[0] == EOFF
+    assert _csr_size([10], 0, 3)[0] == ESHAPE
+    nc = _arr([4])
+    assert lib.dhsa_csr_size(0, nc.ctypes.data, 2, 3, ctypes.byref(ctypes.c_int32()),
+                             ctypes.byref(ctypes.c_int64())) == ESHAPE
+    assert lib.dhsa_csr_size(1, nc.ctypes.data, 2, 3, None, None) == ENULL
+    assert b"NULL" in lib.dhsa_last_error()
+
+
+def test_workspace_sizes():
+    nc = _arr([3, 5])
+    n = ctypes.c_size_t()
+    assert lib.dhsa_mask_workspace_size(2, nc.ctypes.data, 4, 2, 128, ctypes.byref(n)) == OK
+    def al(x):
+        return (x + 255) // 256 * 256
+    assert n.value == al(4 * 8 * 128 * 4) + al(2 * 8 * 128 * 4) + al(4 * (9 + 25) * 4)
+    assert lib.dhsa_mask_workspace_size(2, nc.ctypes.data, 4, 3, 128, ctypes.byref(n)) == ESHAPE
+    assert lib.dhsa_mask_workspace_size(2, nc.ctypes.data, 4, 2, 64, ctypes.byref(n)) == ESHAPE
+    offs = _arr([0, 100, 300, 301, 0, 1, 2, 129, 256, 301])
+    nc2 = _arr([3, 5])
+    assert lib.dhsa_prefill_workspace_size(2, 301, nc2.ctypes.data, offs.ctypes.data,
+                                           ctypes.byref(n)) == OK
+    tiles = (1 + 2 + 1) + (1 + 1 + 1 + 1 + 1)
+    assert n.value == al(tiles * 16)
+
+
+FAKE = 0x10000  # stand-in device address; never dereferenced on these paths
+
+
+def _build_mask(**kw):
+    a = dict(q=FAKE, k=FAKE, batch=1, seq_len=100, hq=4, hkv=2, hd=128,
+             nc=[3], offs=[0, 10, 50, 100], offs_dev=FAKE, topk=2, row_ptr=FAKE, col_idx=FAKE,
+             cap=1 << 20, scores=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    nc = _arr(a["nc"])
+    offs = _arr(a["offs"])
+    return lib.dhsa_build_mask(a["q"], a["k"], a["batch"], a["seq_len"], a["hq"], a["hkv"],
+                               a["hd"], nc.ctypes.data, offs.ctypes.data, a["offs_dev"],
+                               a["topk"], a["row_ptr"], a["col_idx"], a["cap"], a["scores"],
+                               a["ws"], a["ws_bytes"], None)
+
+
+@cpu_only
+def test_build_mask_rejects_bad_arguments():
+    assert _build_mask(q=None) == ENULL
+    assert _build_mask(ws=None) == ENULL
+    assert _build_mask(hd=64) == ESHAPE
+    assert _build_mask(hkv=3) == ESHAPE
+    assert _build_mask(batch=0, nc=[]) == ESHAPE
+    assert _build_mask(offs=[0, 10, 10, 100]) == EOFF       # empty chunk
+    assert _build_mask(offs=[1, 10, 50, 100]) == EOFF       # does not start at 0
+    assert _build_mask(offs=[0, 10, 50, 99]) == EOFF        # does not end at L
+    assert _build_mask(offs=[0, 50, 10, 100]) == EOFF       # decreasing
+    assert _build_mask(topk=0) == ETOPK
+    assert _build_mask(cap=3) == ECAP                       # nnz = 4 * (1 + 2 + 2) = 20
+    assert _build_mask(ws_bytes=16) == ECAP
+    assert _build_mask(ws=FAKE + 8) == ECAP                 # misaligned workspace
+    C = 2049
+    assert _build_mask(seq_len=C, nc=[C], offs=list(range(C + 1))) == EUNSUP
+    assert b"chunks" in lib.dhsa_last_error()
+
+
+def _prefill(**kw):
+    a = dict(batch=1, seq_len=100, hq=4, hkv=2, hd=128, nc=[3], offs=[0, 10, 50, 100],
+             row_ptr=FAKE, col_idx=FAKE, nnz=20, scale=0.0, out=FAKE, lse=None, ws=FAKE,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    nc = _arr(a["nc"])
+    offs = _arr(a["offs"])
+    return lib.dhsa_sparse_prefill(FAKE, FAKE, FAKE, a["batch"], a["seq_len"], a["hq"], a["hkv"],
+                                   a["hd"], nc.ctypes.data, offs.ctypes.data, FAKE, a["row_ptr"],
+                                   a["col_idx"], a["nnz"], a["scale"], a["out"], a["lse"],
+                                   a["ws"], a["ws_bytes"], None)
+
+
+@cpu_only
+def test_sparse_prefill_rejects_bad_arguments():
+    assert _prefill(out=None) == ENULL
+    assert _prefill(row_ptr=None) == ENULL
+    assert _prefill(nnz=-1) == ECSR
+    assert _prefill(hd=256) == ESHAPE
+    assert _prefill(hq=5) == ESHAPE
+    assert _prefill(offs=[0, 10, 50, 101]) == EOFF
+    assert _prefill(scale=float("nan")) == ESHAPE
+    assert _prefill(scale=float("inf")) == ESHAPE
+    assert _prefill(ws_bytes=8) == ECAP
+
+
+@cpu_only
+def test_stage_calls_reject_bad_arguments():
+    nc = _arr([3])
+    offs = _arr([0, 10, 50, 100])
+    assert lib.dhsa_pool(None, 1, 100, 4, 128, nc.ctypes.data, offs.ctypes.data, FAKE, FAKE,
+                         None) == ENULL
+    assert lib.dhsa_pool(FAKE, 1, 100, 4, 128, nc.ctypes.data, _arr([0, 10, 50, 90]).ctypes.data,
+                         FAKE, FAKE, None) == EOFF
+    assert lib.dhsa_chunk_scores(FAKE, FAKE, 1, 4, 3, 128, nc.ctypes.data, FAKE, None) == ESHAPE
+    assert lib.dhsa_topk_csr(FAKE, 1, 4, nc.ctypes.data, 0, FAKE, FAKE, 100, None) == ETOPK
+    assert lib.dhsa_topk_csr(FAKE, 1, 4, nc.ctypes.data, 2, FAKE, FAKE, 1, None) == ECAP
