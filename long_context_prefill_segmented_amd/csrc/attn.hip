@@ -13,21 +13,29 @@
 //
 // Work decomposition (gfx950, wave64):
 //  * a workgroup = 4 waves = 128 query rows of ONE query chunk and ONE query
-//    head; each wave owns 32 rows;
+//    head; each wave owns 32 rows; two workgroups share a CU;
 //  * the kept chunks of the row are concatenated into one gathered key
 //    stream (a prefix table in LDS maps stream positions to tokens), cut
 //    into 64-key sub-tiles that may cross chunk boundaries, so short chunks
 //    waste no MFMA work on padding;
-//  * per sub-tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as
-//    the A operand, Q held in registers as the B operand), so each lane owns
-//    the scores of one query; the running max / sum live per lane; P^T is
-//    rounded to bf16 in registers and feeds O^T += V^T P^T directly as the
-//    B operand.  V is stored transposed in LDS with the key order permuted
-//    (bits 2 and 3 of the key index swapped) so that each A-operand read is
-//    one 16-byte LDS load;
+//  * K and V sub-tiles go straight from global memory into LDS
+//    (global_load_lds, 16 bytes per lane, no staging registers), double
+//    buffered: the loads of sub-tile j+1 are in flight while sub-tile j is
+//    computed, with one barrier per sub-tile.  Both tiles are row-major
+//    [64 keys][128 dims] with the 16-byte chunks of each row XOR-swizzled so
+//    that the MFMA operand reads hit distinct LDS banks;
+//  * per sub-tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K rows from LDS
+//    as the A operand, Q held in registers as the B operand), so each lane
+//    owns the scores of one query and the running max / sum live per lane;
+//    P^T is rounded to bf16 in registers and feeds O^T += V^T P^T directly as
+//    the B operand; the V^T operand is read with the LDS transpose read
+//    (ds_read_b64_tr_b16) from the row-major V tile;
+//  * the running max is updated lazily: the output is rescaled only when the
+//    max grows by more than 2^8, which keeps every p <= 256 and leaves the
+//    normalised result unchanged;
 //  * only the diagonal chunk needs the token-causal test (every earlier
 //    kept chunk lies entirely before the query chunk), and its key range is
-//    cut at the tile's last query row.
+//    cut at the tile's last query row;
 //  * workgroups are renumbered so that each XCD (own L2) works on a
 //    contiguous range of (KV head, query tile) pairs, keeping one KV head's
 //    K/V hot in that XCD's L2.
@@ -39,12 +47,15 @@ namespace dhsa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define DHSA_GLOBAL __attribute__((address_space(1)))
+#define DHSA_LDS __attribute__((address_space(3)))
 
-constexpr int kKStride = kHeadDim + 8;  // bf16 per K row in LDS (272 B)
-constexpr int kVStride = kBlockN + 8;   // bf16 per V^T row in LDS (144 B)
-constexpr int kTable = 512;             // kept chunks per table window
+constexpr int kTileElems = kBlockN * kHeadDim;  // one K or V sub-tile (bf16)
+constexpr int kTable = 512;                      // kept chunks per table window
 constexpr int kNumXcd = 8;
+constexpr float kLazyRescale = 8.0f;             // log2 of the largest p allowed
 
 __device__ __forceinline__ int xcd_remap(int w, int W) {
   const int q = W / kNumXcd, r = W % kNumXcd;
@@ -58,9 +69,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p, SeqTable st) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlockN * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kVStride];
+// LDS tile layout: element (row, d) of a [64][128] bf16 tile sits at
+//   row * 128 + 8 * (chunk ^ swz(row)) + d % 8,   chunk = d / 8,
+// with swz_k(row) = row & 15 for K and swz_v(row) = (row & 3) << 2 for V.
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
+
+// Position -> token walk over the LDS prefix table (positions only grow).
+struct Cursor {
+  int cur, beg, pref, end;
+};
+
+__device__ __forceinline__ int cursor_token(Cursor& c, int pos, const int* tbl_start,
+                                            const int* tbl_pref) {
+  while (pos >= c.end) {
+    ++c.cur;
+    c.beg = tbl_start[c.cur];
+    c.pref = tbl_pref[c.cur];
+    c.end = tbl_pref[c.cur + 1];
+  }
+  return c.beg + (pos - c.pref);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable st) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kTileElems];
   __shared__ int tbl_start[kTable];
   __shared__ int tbl_pref[kTable + 1];
   __shared__ int wsum[4];
@@ -117,22 +150,22 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p, SeqTable st
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) oacc[db][rr] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;  // running max of scale*log2(e)*s, per query
+  float l_run = 0.f;        // this lane's share of the running sum
+  const float c2 = p.scale_log2;
 
   const size_t kv_rs = (size_t)p.hkv * kHeadDim;
   const uint16_t* kbase = p.k + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim;
   const uint16_t* vbase = p.v + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim;
 
-  // loader role: 4 consecutive keys x 8 dims per thread
-  const int kg = tid >> 4;
-  const int dc = tid & 15;
-  const int key0 = 4 * kg;
-  const int vpos0 = (key0 & ~12) | ((key0 & 4) << 1) | ((key0 & 8) >> 1);
+  // loader role: lane fills 16 bytes (physical chunk lane & 15) of rows
+  // 16*wv + 4*u + lane/16, u = 0..3, of each tile
+  const int ld_row0 = 16 * wv + (lane >> 4);
+  const int ld_pc = lane & 15;
 
   for (int64_t wb = e0; wb < e1; wb += kTable) {
     const int nent = (int)((e1 - wb) < kTable ? (e1 - wb) : kTable);
-    __syncthreads();  // the previous window's table is no longer read
+    __syncthreads();  // the previous window's table and tiles are no longer read
     int len2[2], beg2[2];
     int diag_u = -1;
 #pragma unroll
@@ -187,50 +220,39 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p, SeqTable st
     const int Gtot = total;
     const int Gd0 = s_diag[0];
     const int Gd1 = s_diag[1];
+    if (Gtot == 0) continue;
 
-    int cur = 0;
-    for (int p0 = 0; p0 < Gtot; p0 += kBlockN) {
-      // ---- gather K/V rows of stream positions p0 + 4kg + u
-      uint4 kr[4], vr[4];
+    Cursor cur{-1, 0, 0, 0};
+    // issue the direct-to-LDS loads of the sub-tile at stream position pp
+    auto issue = [&](int pp, int buf) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int pos = p0 + key0 + u;
-        if (pos < Gtot) {
-          while (tbl_pref[cur + 1] <= pos) ++cur;
-          const int s = tbl_start[cur] + (pos - tbl_pref[cur]);
-          kr[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)s * kv_rs + 8 * dc);
-          vr[u] = *reinterpret_cast<const uint4*>(vbase + (size_t)s * kv_rs + 8 * dc);
-        } else {
-          kr[u] = make_uint4(0, 0, 0, 0);
-          vr[u] = make_uint4(0, 0, 0, 0);
-        }
+        const int row = ld_row0 + 4 * u;
+        const int pos = pp + row;
+        const int tok = pos < Gtot ? cursor_token(cur, pos, tbl_start, tbl_pref) : 0;
+        const uint16_t* ks = kbase + (size_t)tok * kv_rs + 8 * (ld_pc ^ swz_k(row));
+        const uint16_t* vs = vbase + (size_t)tok * kv_rs + 8 * (ld_pc ^ swz_v(row));
+        uint16_t* kd = &Ks[buf][(16 * wv + 4 * u) * kHeadDim];
+        uint16_t* vd = &Vs[buf][(16 * wv + 4 * u) * kHeadDim];
+        __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)ks, (DHSA_LDS void*)kd, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)vs, (DHSA_LDS void*)vd, 16, 0, 0);
       }
-      __syncthreads();  // the previous sub-tile's LDS reads are done
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        *reinterpret_cast<uint4*>(&Ks[(key0 + u) * kKStride + 8 * dc]) = kr[u];
-      {
-        const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
-        const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
-        const uint32_t w2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
-        const uint32_t w3[4] = {vr[3].x, vr[3].y, vr[3].z, vr[3].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // dims 2e (low halves) and 2e+1 (high halves) of keys key0..key0+3
-          const uint32_t lo01 = (w0[e] & 0xffffu) | (w1[e] << 16);
-          const uint32_t lo23 = (w2[e] & 0xffffu) | (w3[e] << 16);
-          const uint32_t hi01 = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-          const uint32_t hi23 = (w2[e] >> 16) | (w3[e] & 0xffff0000u);
-          *reinterpret_cast<uint2*>(&Vt[(8 * dc + 2 * e) * kVStride + vpos0]) = make_uint2(lo01, lo23);
-          *reinterpret_cast<uint2*>(&Vt[(8 * dc + 2 * e + 1) * kVStride + vpos0]) = make_uint2(hi01, hi23);
-        }
-      }
-      __syncthreads();
+    };
+
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int buf = 0;
+    for (int p0 = 0; p0 < Gtot; p0 += kBlockN, buf ^= 1) {
+      if (p0 + kBlockN < Gtot) issue(p0 + kBlockN, buf ^ 1);
 
       // a wave skips a sub-tile that lies inside the diagonal chunk beyond
       // all of its query rows
-      const bool skip = (p0 >= Gd0) && (p0 + kBlockN <= Gd1) && (p0 - Gd0 > q0 + wv * 32 + 31);
+      const bool skip = (p0 >= Gd0) && (p0 + kBlockN <= Gd1 || Gd1 >= Gtot) &&
+                        (p0 - Gd0 > q0 + wv * 32 + 31);
       if (wave_active && !skip) {
+        const uint16_t* Kt = Ks[buf];
+        const uint16_t* Vt = Vs[buf];
         f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -240,63 +262,86 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p, SeqTable st
         for (int ds = 0; ds < 8; ++ds) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8_t a =
-                *reinterpret_cast<const bf16x8_t*>(&Ks[(kb * 32 + l32) * kKStride + ds * 16 + hl * 8]);
+            const int row = kb * 32 + l32;
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+                &Kt[row * kHeadDim + 8 * ((2 * ds + hl) ^ swz_k(row))]);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc[kb], 0, 0, 0);
           }
         }
-        // scale, mask, running max (accumulator: lane -> query, register rr
-        // -> key 8*(rr/4) + 4*(lane/32) + rr%4 of the 32-key block)
+        // mask, running max (accumulator: lane -> query, register rr -> key
+        // 8*(rr/4) + 4*(lane/32) + rr%4 of the 32-key block)
         const bool need_mask = (p0 + kBlockN > Gtot) || (p0 + kBlockN > Gd0 && p0 < Gd1);
-        float mx = -INFINITY;
+        if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            float sv = sacc[kb][rr] * p.scale_log2;
-            if (need_mask) {
+            for (int rr = 0; rr < 16; ++rr) {
               const int pos = p0 + kb * 32 + 8 * (rr >> 2) + 4 * hl + (rr & 3);
               const bool vis = pos < Gtot && (pos < Gd0 || pos >= Gd1 || pos - Gd0 <= qrow);
-              sv = vis ? sv : -INFINITY;
+              sacc[kb][rr] = vis ? sacc[kb][rr] : -INFINITY;
             }
-            sacc[kb][rr] = sv;
-            mx = fmaxf(mx, sv);
           }
         }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[kb][rr]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
+        const float mxs = mx * c2;
+        const bool upd = mxs > m_run + kLazyRescale;
+        if (__ballot(upd)) {
+          const float alpha = upd ? fast_exp2(m_run - mxs) : 1.0f;
+          m_run = upd ? mxs : m_run;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) oacc[db][rr] *= alpha;
+        }
+        const float mneg = m_run == -INFINITY ? 0.f : -m_run;
         float lsum = 0.f;
         bf16x8_t pk[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
-            const float pv = fast_exp2(sacc[kb][rr] - m_use);
+            const float pv = fast_exp2(__builtin_fmaf(sacc[kb][rr], c2, mneg));
             lsum += pv;
             pk[kb][rr >> 3][rr & 7] = (__bf16)pv;
           }
         }
-        l_run = l_run * alpha + lsum;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) oacc[db][rr] *= alpha;
+        l_run += lsum;
+        // O^T += V^T P^T.  A operand (V^T) for 16 keys: two transpose reads,
+        // lane 16*G + s of read a reads 4 dims of key
+        //   kb*32 + 16*hh + 8*a + 4*(G/2) + s/4, dims db*32 + 16*(G%2) + 4*(s%4)
+        const int G16 = lane >> 4;
+        const int s16 = lane & 15;
+        const int vkey_off = 4 * (G16 >> 1) + (s16 >> 2);
+        const int vd_off = 16 * (G16 & 1) + 4 * (s16 & 3);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-              const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-                  &Vt[(db * 32 + l32) * kVStride + kb * 32 + 16 * hh + 8 * hl]);
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kb][hh], oacc[db], 0, 0, 0);
+              bf16x4_t part[2];
+#pragma unroll
+              for (int a = 0; a < 2; ++a) {
+                const int key = kb * 32 + 16 * hh + 8 * a + vkey_off;
+                const int d = db * 32 + vd_off;
+                const int idx = key * kHeadDim + 8 * ((d >> 3) ^ swz_v(key)) + (d & 7);
+                part[a] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (DHSA_LDS bf16x4_t*)(&Vt[idx]));
+              }
+              const bf16x8_t va = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[kb][hh], oacc[db], 0, 0, 0);
             }
           }
         }
       }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into buf^1 have landed
+      __syncthreads();
     }
   }
 
