@@ -48,6 +48,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define DHSA_GLOBAL __attribute__((address_space(1)))
 #define DHSA_LDS __attribute__((address_space(3)))
@@ -154,14 +155,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
   float l_run = 0.f;        // this lane's share of the running sum
   const float c2 = p.scale_log2;
 
+  // K/V of KV head g: row t starts at byte t * rowbytes from these bases
+  const uint32_t rowbytes = (uint32_t)p.hkv * kHeadDim * 2;
   const size_t kv_rs = (size_t)p.hkv * kHeadDim;
-  const uint16_t* kbase = p.k + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim;
-  const uint16_t* vbase = p.v + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim;
+  const char* kbytes = reinterpret_cast<const char*>(p.k + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim);
+  const char* vbytes = reinterpret_cast<const char*>(p.v + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim);
 
-  // loader role: lane fills 16 bytes (physical chunk lane & 15) of rows
-  // 16*wv + 4*u + lane/16, u = 0..3, of each tile
-  const int ld_row0 = 16 * wv + (lane >> 4);
-  const int ld_pc = lane & 15;
+  // loader role: instruction u of wave wv fills tile rows 16*wv + 4*u + lane/16,
+  // lane & 15 being the physical 16-byte chunk; the lane also walks the token
+  // of stream row 16*wv + (lane & 15) and hands it to the lanes that load it
+  const int lsub = lane & 15;
+  const int lgrp = lane >> 4;
+  uint32_t kchunk[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kchunk[u] = 16u * (uint32_t)(lsub ^ swz_k(4 * u + lgrp));
+  const uint32_t vchunk = 16u * (uint32_t)(lsub ^ swz_v(lgrp));
+
+  // V^T operand reads: lane 16*G + s of transpose read a covers 4 dims of key
+  //   kb*32 + 16*hh + 8*a + 4*(G/2) + s/4, dims db*32 + 16*(G%2) + 4*(s%4)
+  const int vkey_off = 4 * (lgrp >> 1) + (lsub >> 2);
+  const int vd_off = 16 * (lgrp & 1) + 4 * (lsub & 3);
+  const int qmin = q0 + wv * 32;  // first query row (chunk-local) of this wave
+  constexpr int kNoDiag = 0x3fffffff;
 
   for (int64_t wb = e0; wb < e1; wb += kTable) {
     const int nent = (int)((e1 - wb) < kTable ? (e1 - wb) : kTable);
@@ -194,8 +209,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
     }
     if (lane == 63) wsum[wv] = incl;
     if (tid == 0) {
-      s_diag[0] = INT_MAX;
-      s_diag[1] = INT_MAX;
+      s_diag[0] = kNoDiag;
+      s_diag[1] = kNoDiag;
     }
     __syncthreads();
     int wpre = 0;
@@ -223,19 +238,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
     if (Gtot == 0) continue;
 
     Cursor cur{-1, 0, 0, 0};
-    // issue the direct-to-LDS loads of the sub-tile at stream position pp
+    // direct-to-LDS loads of the sub-tile at stream position pp into buf
     auto issue = [&](int pp, int buf) {
+      const int pos = pp + 16 * wv + lsub;
+      const int tok = pos < Gtot ? cursor_token(cur, pos, tbl_start, tbl_pref) : 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int row = ld_row0 + 4 * u;
-        const int pos = pp + row;
-        const int tok = pos < Gtot ? cursor_token(cur, pos, tbl_start, tbl_pref) : 0;
-        const uint16_t* ks = kbase + (size_t)tok * kv_rs + 8 * (ld_pc ^ swz_k(row));
-        const uint16_t* vs = vbase + (size_t)tok * kv_rs + 8 * (ld_pc ^ swz_v(row));
+        const uint32_t tk = (uint32_t)__shfl(tok, 4 * u + lgrp, 64);
+        const uint32_t rb = tk * rowbytes;
         uint16_t* kd = &Ks[buf][(16 * wv + 4 * u) * kHeadDim];
         uint16_t* vd = &Vs[buf][(16 * wv + 4 * u) * kHeadDim];
-        __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)ks, (DHSA_LDS void*)kd, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)vs, (DHSA_LDS void*)vd, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)(kbytes + (rb + kchunk[u])),
+                                         (DHSA_LDS void*)kd, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)(vbytes + (rb + vchunk)),
+                                         (DHSA_LDS void*)vd, 16, 0, 0);
       }
     };
 
@@ -244,41 +260,64 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
     __syncthreads();
     int buf = 0;
     for (int p0 = 0; p0 < Gtot; p0 += kBlockN, buf ^= 1) {
-      if (p0 + kBlockN < Gtot) issue(p0 + kBlockN, buf ^ 1);
-
+      const bool has_next = p0 + kBlockN < Gtot;
       // a wave skips a sub-tile that lies inside the diagonal chunk beyond
       // all of its query rows
       const bool skip = (p0 >= Gd0) && (p0 + kBlockN <= Gd1 || Gd1 >= Gtot) &&
-                        (p0 - Gd0 > q0 + wv * 32 + 31);
+                        (p0 - Gd0 > qmin + 31);
       if (wave_active && !skip) {
         const uint16_t* Kt = Ks[buf];
         const uint16_t* Vt = Vs[buf];
+        // ---- S^T = K Q^T, K operand reads one step ahead of the MFMAs
         f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) sacc[kb][rr] = 0.f;
+        bf16x8_t kcur[2], knext[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = kb * 32 + l32;
+          kcur[kb] = *reinterpret_cast<const bf16x8_t*>(&Kt[row * kHeadDim + 8 * (hl ^ swz_k(row))]);
+        }
 #pragma unroll
         for (int ds = 0; ds < 8; ++ds) {
+          if (ds + 1 < 8) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const int row = kb * 32 + l32;
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-                &Kt[row * kHeadDim + 8 * ((2 * ds + hl) ^ swz_k(row))]);
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc[kb], 0, 0, 0);
+            for (int kb = 0; kb < 2; ++kb) {
+              const int row = kb * 32 + l32;
+              knext[kb] = *reinterpret_cast<const bf16x8_t*>(
+                  &Kt[row * kHeadDim + 8 * ((2 * ds + 2 + hl) ^ swz_k(row))]);
+            }
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[kb], qf[ds], sacc[kb], 0, 0, 0);
+          if (ds + 1 < 8) {
+            kcur[0] = knext[0];
+            kcur[1] = knext[1];
           }
         }
-        // mask, running max (accumulator: lane -> query, register rr -> key
-        // 8*(rr/4) + 4*(lane/32) + rr%4 of the 32-key block)
-        const bool need_mask = (p0 + kBlockN > Gtot) || (p0 + kBlockN > Gd0 && p0 < Gd1);
+        // the next sub-tile's loads go out while the MFMAs run
+        if (has_next) issue(p0 + kBlockN, buf ^ 1);
+
+        // ---- mask: only the tail of the stream and the part of the diagonal
+        // chunk past this wave's first query row can hold hidden keys
+        // (accumulator: lane -> query, register rr -> key
+        //  8*(rr/4) + 4*(lane/32) + rr%4 of the 32-key block)
+        const bool need_mask =
+            (p0 + kBlockN > Gtot) || (p0 + kBlockN > Gd0 + qmin + 1 && p0 < Gd1);
         if (need_mask) {
+          const int rel_tot = Gtot - p0;
+          const int rel_lo = Gd0 + qrow - p0;
+          const int rel_hi = Gd1 - p0;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-              const int pos = p0 + kb * 32 + 8 * (rr >> 2) + 4 * hl + (rr & 3);
-              const bool vis = pos < Gtot && (pos < Gd0 || pos >= Gd1 || pos - Gd0 <= qrow);
-              sacc[kb][rr] = vis ? sacc[kb][rr] : -INFINITY;
+              const int rel = kb * 32 + 8 * (rr >> 2) + 4 * hl + (rr & 3);
+              const bool hidden = (rel >= rel_tot) | ((rel > rel_lo) & (rel < rel_hi));
+              sacc[kb][rr] = hidden ? -INFINITY : sacc[kb][rr];
             }
           }
         }
@@ -299,30 +338,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) oacc[db][rr] *= alpha;
         }
+        // ---- P^T = exp2(c2 * s - m) in bf16; the row sum adds the rounded
+        // values (the weights the PV product actually uses) two at a time
         const float mneg = m_run == -INFINITY ? 0.f : -m_run;
-        float lsum = 0.f;
-        bf16x8_t pk[2][2];
+        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+        bf16x2_t pp[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const float pv = fast_exp2(__builtin_fmaf(sacc[kb][rr], c2, mneg));
-            lsum += pv;
-            pk[kb][rr >> 3][rr & 7] = (__bf16)pv;
+          for (int e = 0; e < 8; ++e) {
+            const float p0v = fast_exp2(__builtin_fmaf(sacc[kb][2 * e], c2, mneg));
+            const float p1v = fast_exp2(__builtin_fmaf(sacc[kb][2 * e + 1], c2, mneg));
+            pp[kb][e] = bf16x2_t{(__bf16)p0v, (__bf16)p1v};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[kb][e], ones, l_run, false);
           }
         }
-        l_run += lsum;
-        // O^T += V^T P^T.  A operand (V^T) for 16 keys: two transpose reads,
-        // lane 16*G + s of read a reads 4 dims of key
-        //   kb*32 + 16*hh + 8*a + 4*(G/2) + s/4, dims db*32 + 16*(G%2) + 4*(s%4)
-        const int G16 = lane >> 4;
-        const int s16 = lane & 15;
-        const int vkey_off = 4 * (G16 >> 1) + (s16 >> 2);
-        const int vd_off = 16 * (G16 & 1) + 4 * (s16 & 3);
+        // ---- O^T += V^T P^T
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8_t pk = __builtin_shufflevector(
+                __builtin_shufflevector(pp[kb][4 * hh], pp[kb][4 * hh + 1], 0, 1, 2, 3),
+                __builtin_shufflevector(pp[kb][4 * hh + 2], pp[kb][4 * hh + 3], 0, 1, 2, 3),
+                0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
               bf16x4_t part[2];
@@ -331,14 +370,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
                 const int key = kb * 32 + 16 * hh + 8 * a + vkey_off;
                 const int d = db * 32 + vd_off;
                 const int idx = key * kHeadDim + 8 * ((d >> 3) ^ swz_v(key)) + (d & 7);
-                part[a] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (DHSA_LDS bf16x4_t*)(&Vt[idx]));
+                part[a] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DHSA_LDS bf16x4_t*)(&Vt[idx]));
               }
               const bf16x8_t va = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[kb][hh], oacc[db], 0, 0, 0);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk, oacc[db], 0, 0, 0);
             }
           }
         }
+      } else if (has_next) {
+        issue(p0 + kBlockN, buf ^ 1);
       }
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into buf^1 have landed
       __syncthreads();

@@ -21,7 +21,9 @@ import numpy as np
 # device memory and streams are valid in the library's calls.
 import torch  # noqa: E402,F401  (must precede the CDLL below)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdhsa.so")
+# DHSA_LIBRARY may name another build of the same library (e.g. a debug build)
+LIB_PATH = os.environ.get("DHSA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libdhsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
