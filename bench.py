@@ -63,7 +63,7 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(x, rows_gpu_unused, hq, hkv, budget_rows=24, seed=0):
+def cpu_baseline(x, rows_gpu_unused, hq, hkv, budget_rows=1500, seed=0):
     """The oracle, untuned, on a bounded sample of the layer: full-layer mask
     construction plus attention for a seeded sample of (head, query chunk)
     rows, scaled to kept-tile TFLOP/s."""
