@@ -92,12 +92,32 @@ __device__ __forceinline__ int cursor_token(Cursor& c, int pos, const int* tbl_s
   return c.beg + (pos - c.pref);
 }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable st) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kTileElems];
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqTable st) {
+  constexpr int kBlockM = 32 * NW;               // query rows per workgroup
+  constexpr int kRowsPerWave = kBlockN / NW;     // tile rows each wave loads
+  constexpr int kLoadsPerMat = kRowsPerWave / 4; // 1 KB direct loads per wave per matrix
+  constexpr int kEntPerThread = kTable / (64 * NW);
+  static_assert(kLoadsPerMat >= 1 && kEntPerThread >= 1, "shape");
+  // two K and two V buffers as distinct LDS objects; the sub-tile loop is
+  // unrolled by two, so every access names its buffer statically and the
+  // compiler can tell the in-flight direct loads into the other pair from
+  // the reads of the current one (it does not wait for them)
+  __shared__ __attribute__((aligned(16))) uint16_t K0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[kTileElems];
   __shared__ int tbl_start[kTable];
   __shared__ int tbl_pref[kTable + 1];
-  __shared__ int wsum[4];
+  __shared__ int wsum[NW];
   __shared__ int s_diag[2];
 
   const int tid = threadIdx.x;
@@ -161,14 +181,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
   const char* kbytes = reinterpret_cast<const char*>(p.k + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim);
   const char* vbytes = reinterpret_cast<const char*>(p.v + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim);
 
-  // loader role: instruction u of wave wv fills tile rows 16*wv + 4*u + lane/16,
-  // lane & 15 being the physical 16-byte chunk; the lane also walks the token
-  // of stream row 16*wv + (lane & 15) and hands it to the lanes that load it
+  // loader role: direct load u of wave wv fills tile rows
+  // kRowsPerWave*wv + 4*u + lane/16, lane & 15 being the physical 16-byte
+  // chunk; lane & (kRowsPerWave-1) walks the token of stream row
+  // kRowsPerWave*wv + that and hands it to the lanes that load the row
   const int lsub = lane & 15;
   const int lgrp = lane >> 4;
-  uint32_t kchunk[4];
+  const int lwalk = lane & (kRowsPerWave - 1);
+  uint32_t kchunk[kLoadsPerMat];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) kchunk[u] = 16u * (uint32_t)(lsub ^ swz_k(4 * u + lgrp));
+  for (int u = 0; u < kLoadsPerMat; ++u)
+    kchunk[u] = 16u * (uint32_t)(lsub ^ swz_k(kRowsPerWave * wv + 4 * u + lgrp));
   const uint32_t vchunk = 16u * (uint32_t)(lsub ^ swz_v(lgrp));
 
   // V^T operand reads: lane 16*G + s of transpose read a covers 4 dims of key
@@ -181,26 +204,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
   for (int64_t wb = e0; wb < e1; wb += kTable) {
     const int nent = (int)((e1 - wb) < kTable ? (e1 - wb) : kTable);
     __syncthreads();  // the previous window's table and tiles are no longer read
-    int len2[2], beg2[2];
+    int lenv[kEntPerThread], begv[kEntPerThread];
     int diag_u = -1;
+    int loc = 0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = 2 * tid + u;
-      len2[u] = 0;
-      beg2[u] = 0;
+    for (int u = 0; u < kEntPerThread; ++u) {
+      const int idx = kEntPerThread * tid + u;
+      lenv[u] = 0;
+      begv[u] = 0;
       if (idx < nent) {
         const int j = p.col_idx[wb + idx];
         if (j >= 0 && j <= i) {
-          beg2[u] = p.offs[obase + j];
-          len2[u] = p.offs[obase + j + 1] - beg2[u];
+          begv[u] = p.offs[obase + j];
+          lenv[u] = p.offs[obase + j + 1] - begv[u];
           if (j == i) {
-            len2[u] = min(len2[u], q0 + rows);
+            lenv[u] = min(lenv[u], q0 + rows);
             diag_u = u;
           }
         }
       }
+      loc += lenv[u];
     }
-    const int loc = len2[0] + len2[1];
     int incl = loc;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -213,22 +237,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
       s_diag[1] = kNoDiag;
     }
     __syncthreads();
-    int wpre = 0;
-    for (int x = 0; x < wv; ++x) wpre += wsum[x];
-    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    const int excl = wpre + incl - loc;
-    if (2 * tid < nent) {
-      tbl_start[2 * tid] = beg2[0];
-      tbl_pref[2 * tid] = excl;
+    int wpre = 0, total = 0;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+      wpre += x < wv ? wsum[x] : 0;
+      total += wsum[x];
     }
-    if (2 * tid + 1 < nent) {
-      tbl_start[2 * tid + 1] = beg2[1];
-      tbl_pref[2 * tid + 1] = excl + len2[0];
-    }
-    if (diag_u >= 0) {
-      const int gs = excl + (diag_u ? len2[0] : 0);
-      s_diag[0] = gs;
-      s_diag[1] = gs + len2[diag_u];
+    int run = wpre + incl - loc;
+#pragma unroll
+    for (int u = 0; u < kEntPerThread; ++u) {
+      const int idx = kEntPerThread * tid + u;
+      if (idx < nent) {
+        tbl_start[idx] = begv[u];
+        tbl_pref[idx] = run;
+      }
+      if (u == diag_u) {
+        s_diag[0] = run;
+        s_diag[1] = run + lenv[u];
+      }
+      run += lenv[u];
     }
     if (tid == 0) tbl_pref[nent] = total;
     __syncthreads();
@@ -236,18 +263,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
     const int Gd0 = s_diag[0];
     const int Gd1 = s_diag[1];
     if (Gtot == 0) continue;
+    const int nsub = (Gtot + kBlockN - 1) / kBlockN;
 
     Cursor cur{-1, 0, 0, 0};
-    // direct-to-LDS loads of the sub-tile at stream position pp into buf
-    auto issue = [&](int pp, int buf) {
-      const int pos = pp + 16 * wv + lsub;
+    // direct-to-LDS loads of sub-tile js into (Kd, Vd)
+    auto issue = [&](int js, uint16_t* Kd, uint16_t* Vd) {
+      const int pos = js * kBlockN + kRowsPerWave * wv + lwalk;
       const int tok = pos < Gtot ? cursor_token(cur, pos, tbl_start, tbl_pref) : 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kLoadsPerMat; ++u) {
         const uint32_t tk = (uint32_t)__shfl(tok, 4 * u + lgrp, 64);
         const uint32_t rb = tk * rowbytes;
-        uint16_t* kd = &Ks[buf][(16 * wv + 4 * u) * kHeadDim];
-        uint16_t* vd = &Vs[buf][(16 * wv + 4 * u) * kHeadDim];
+        uint16_t* kd = Kd + (kRowsPerWave * wv + 4 * u) * kHeadDim;
+        uint16_t* vd = Vd + (kRowsPerWave * wv + 4 * u) * kHeadDim;
         __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)(kbytes + (rb + kchunk[u])),
                                          (DHSA_LDS void*)kd, 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)(vbytes + (rb + vchunk)),
@@ -255,19 +283,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
       }
     };
 
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int buf = 0;
-    for (int p0 = 0; p0 < Gtot; p0 += kBlockN, buf ^= 1) {
-      const bool has_next = p0 + kBlockN < Gtot;
+    // one sub-tile js: compute on (Kt, Vt) while sub-tile js+1 streams into
+    // (Kn, Vn), the buffers of sub-tile js-1
+    auto subtile = [&](int js, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
+      const int p0 = js * kBlockN;
+      if (js + 1 < nsub) issue(js + 1, Kn, Vn);
       // a wave skips a sub-tile that lies inside the diagonal chunk beyond
       // all of its query rows
       const bool skip = (p0 >= Gd0) && (p0 + kBlockN <= Gd1 || Gd1 >= Gtot) &&
                         (p0 - Gd0 > qmin + 31);
       if (wave_active && !skip) {
-        const uint16_t* Kt = Ks[buf];
-        const uint16_t* Vt = Vs[buf];
         // ---- S^T = K Q^T, K operand reads one step ahead of the MFMAs
         f32x16 sacc[2];
 #pragma unroll
@@ -298,8 +323,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
             kcur[1] = knext[1];
           }
         }
-        // the next sub-tile's loads go out while the MFMAs run
-        if (has_next) issue(p0 + kBlockN, buf ^ 1);
 
         // ---- mask: only the tail of the stream and the part of the diagonal
         // chunk past this wave's first query row can hold hidden keys
@@ -377,11 +400,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
             }
           }
         }
-      } else if (has_next) {
-        issue(p0 + kBlockN, buf ^ 1);
       }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into buf^1 have landed
+      wait_vmcnt<0>();  // this wave's loads of sub-tile js+1 have landed
       __syncthreads();
+    };
+
+    issue(0, K0, V0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int js = 0; js < nsub; js += 2) {
+      subtile(js, K0, V0, K1, V1);
+      if (js + 1 < nsub) subtile(js + 1, K1, V1, K0, V0);
     }
   }
 
@@ -414,7 +443,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, SeqTable
 // One workgroup per sequence: expand chunk lengths into the query-tile list
 // (b, chunk, first row) with a block-wide exclusive scan.
 __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restrict__ offs,
-                                                         SeqTable st, int4* __restrict__ tiles) {
+                                                         SeqTable st, int4* __restrict__ tiles,
+                                                         int32_t block_m) {
   __shared__ int wsum[4];
   const int b = blockIdx.x;
   const int C = st.num_chunks[b];
@@ -423,7 +453,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
   int base = st.tbase[b];
   for (int c0 = 0; c0 < C; c0 += 256) {
     const int c = c0 + tid;
-    const int nt = c < C ? (offs[obase + c + 1] - offs[obase + c] + kBlockM - 1) / kBlockM : 0;
+    const int nt = c < C ? (offs[obase + c + 1] - offs[obase + c] + block_m - 1) / block_m : 0;
     int incl = nt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -436,7 +466,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
     for (int x = 0; x < wv; ++x) pre += wsum[x];
     const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     const int ex = base + pre + incl - nt;
-    for (int t = 0; t < nt; ++t) tiles[ex + t] = make_int4(b, c, t * kBlockM, 0);
+    for (int t = 0; t < nt; ++t) tiles[ex + t] = make_int4(b, c, t * block_m, 0);
     base += tot;
     __syncthreads();
   }
@@ -445,16 +475,20 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
 }  // namespace
 
 hipError_t launch_plan_tiles(const int32_t* offs_dev, const SeqTable& st, int4* tiles,
-                             hipStream_t stream) {
+                             int32_t block_m, hipStream_t stream) {
   hipLaunchKernelGGL(plan_tiles_kernel, dim3(st.batch), dim3(256), 0, stream, offs_dev, st,
-                     tiles);
+                     tiles, block_m);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnParams& p, const SeqTable& st, hipStream_t stream) {
   const int64_t grid = (int64_t)p.num_tiles * p.hq;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p, st);
+  if (p.block_m == kBlockMLarge) {
+    hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3((unsigned)grid), dim3(512), 0, stream, p, st);
+  } else {
+    hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, p, st);
+  }
   return hipGetLastError();
 }
 

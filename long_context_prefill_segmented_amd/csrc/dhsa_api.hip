@@ -1,6 +1,7 @@
 // Host side of the C ABI: argument validation, sizes, launch planning.
 // Every check runs before any HIP call; on an error nothing is enqueued.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -118,16 +119,39 @@ int64_t score_tiles(int32_t batch, const int32_t* num_chunks, int32_t hq) {
 }
 
 int64_t query_tiles(int32_t batch, const int32_t* num_chunks, const int32_t* offs,
-                    int32_t* tbase) {
+                    int32_t block_m, int32_t* tbase) {
   int64_t t = 0;
   size_t o = 0;
   for (int b = 0; b < batch; ++b) {
     if (tbase) tbase[b] = (int32_t)t;
     for (int c = 0; c < num_chunks[b]; ++c)
-      t += (offs[o + c + 1] - offs[o + c] + kBlockM - 1) / kBlockM;
+      t += (offs[o + c + 1] - offs[o + c] + block_m - 1) / block_m;
     o += num_chunks[b] + 1;
   }
   return t;
+}
+
+// Query tile height for the attention kernel.  A 256-row tile (8 waves, one
+// workgroup per CU) streams each kept K/V sub-tile for twice as many rows as
+// a 128-row tile, but a chunk's last tile leaves waves idle; the large tile
+// is taken when at least 75 % of its 32-row wave slots hold query rows.
+// DHSA_ATTN_BLOCK_M=128|256 in the environment forces one of them.
+int32_t choose_block_m(int32_t batch, const int32_t* num_chunks, const int32_t* offs) {
+  if (const char* env = getenv("DHSA_ATTN_BLOCK_M")) {
+    const int v = atoi(env);
+    if (v == kBlockMSmall || v == kBlockMLarge) return v;
+  }
+  int64_t waves = 0, slots = 0;
+  size_t o = 0;
+  for (int b = 0; b < batch; ++b) {
+    for (int c = 0; c < num_chunks[b]; ++c) {
+      const int64_t n = offs[o + c + 1] - offs[o + c];
+      waves += (n + 31) / 32;
+      slots += (kBlockMLarge / 32) * ((n + kBlockMLarge - 1) / kBlockMLarge);
+    }
+    o += num_chunks[b] + 1;
+  }
+  return 4 * waves >= 3 * slots ? kBlockMLarge : kBlockMSmall;
 }
 
 int max_chunks(int32_t batch, const int32_t* num_chunks) {
@@ -203,7 +227,9 @@ int dhsa_prefill_workspace_size(int32_t batch, int32_t seq_len, const int32_t* n
   if (s) return s;
   s = check_offsets(batch, seq_len, num_chunks, chunk_offsets);
   if (s) return s;
-  *bytes = align_up((size_t)query_tiles(batch, num_chunks, chunk_offsets, nullptr) * sizeof(int4));
+  // sized for the smaller tile height (the larger needs fewer tiles)
+  *bytes = align_up((size_t)query_tiles(batch, num_chunks, chunk_offsets, kBlockMSmall, nullptr) *
+                    sizeof(int4));
   return ok();
 }
 
@@ -340,7 +366,8 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
     return fail(DHSA_ERR_SHAPE, "softmax_scale is not finite");
   const int32_t ntiles_max = INT32_MAX / num_q_heads;
   int32_t tbase[kMaxBatch];
-  const int64_t ntiles = query_tiles(batch, num_chunks, chunk_offsets, tbase);
+  const int32_t block_m = choose_block_m(batch, num_chunks, chunk_offsets);
+  const int64_t ntiles = query_tiles(batch, num_chunks, chunk_offsets, block_m, tbase);
   if (ntiles > ntiles_max) return fail(DHSA_ERR_UNSUPPORTED, "too many query tiles");
   const size_t need = align_up((size_t)ntiles * sizeof(int4));
   if (workspace_bytes < need)
@@ -353,7 +380,7 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
   for (int b = 0; b < batch; ++b) st.tbase[b] = tbase[b];
   hipStream_t strm = static_cast<hipStream_t>(stream);
   int4* tiles = static_cast<int4*>(workspace);
-  hipError_t e = launch_plan_tiles(chunk_offsets_dev, st, tiles, strm);
+  hipError_t e = launch_plan_tiles(chunk_offsets_dev, st, tiles, block_m, strm);
   if (e != hipSuccess) return hip_fail(e, "tile plan launch");
 
   AttnParams p;
@@ -371,6 +398,7 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
   p.seq_len = seq_len;
   p.hq = num_q_heads;
   p.hkv = num_kv_heads;
+  p.block_m = block_m;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kHeadDim);
   p.scale_log2 = scale * 1.4426950408889634f;
   e = launch_attention(p, st, strm);

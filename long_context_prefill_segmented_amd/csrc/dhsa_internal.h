@@ -12,10 +12,13 @@ constexpr int kHeadDim = DHSA_HEAD_DIM;
 constexpr int kMaxBatch = DHSA_MAX_BATCH;
 constexpr int kMaxChunks = DHSA_MAX_CHUNKS;
 
-// Attention tiling: a workgroup owns kBlockM query rows of one query chunk
-// and one query head (4 waves x 32 rows) and streams the gathered kept keys
-// kBlockN at a time.
-constexpr int kBlockM = 128;
+// Attention tiling: a workgroup of NW waves owns 32 * NW query rows (the
+// query tile) of one query chunk and one query head, and streams the
+// gathered kept keys kBlockN at a time.  Two tile heights are built: 128 rows
+// (4 waves, two workgroups per CU) and 256 rows (8 waves, one per CU; every
+// K/V sub-tile serves twice the rows).
+constexpr int kBlockMSmall = 128;
+constexpr int kBlockMLarge = 256;
 constexpr int kBlockN = 64;
 
 // Per-sequence bookkeeping passed by value in kernel arguments (host
@@ -53,7 +56,7 @@ hipError_t launch_topk(const float* scores, const SeqTable& st, int32_t hq,
                        int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
 
 hipError_t launch_plan_tiles(const int32_t* offs_dev, const SeqTable& st,
-                             int4* tiles, hipStream_t stream);
+                             int4* tiles, int32_t block_m, hipStream_t stream);
 
 struct AttnParams {
   const uint16_t* q;
@@ -70,6 +73,7 @@ struct AttnParams {
   int32_t seq_len;
   int32_t hq;
   int32_t hkv;
+  int32_t block_m;  // query tile height: kBlockMSmall or kBlockMLarge
   float scale_log2;
 };
 

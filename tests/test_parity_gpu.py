@@ -236,8 +236,15 @@ def test_build_mask_matches_oracle_mask(name):
 # ---------------------------------------------------------------- attention
 
 
+@pytest.fixture(params=["128", "256"])
+def block_m(request, monkeypatch):
+    """Runs a test with each query-tile height of the attention kernel."""
+    monkeypatch.setenv("DHSA_ATTN_BLOCK_M", request.param)
+    return int(request.param)
+
+
 @pytest.mark.parametrize("name", list(CASES))
-def test_attention_on_oracle_mask(name):
+def test_attention_on_oracle_mask(name, block_m):
     c = get_case(name)
     csr = dhsa.csr_from_host(c.rp, c.ci)
     say("  sparse_prefill on the oracle mask")
@@ -251,7 +258,7 @@ def test_attention_on_oracle_mask(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured"])
-def test_attention_on_gpu_mask_end_to_end(name):
+def test_attention_on_gpu_mask_end_to_end(name, block_m):
     c = get_case(name)
     csr = dhsa.build_mask(c.q, c.k, c.offs, c.topk)
     out = dhsa.sparse_prefill(c.q, c.k, c.v, c.offs, csr)
@@ -283,7 +290,7 @@ def test_unit_chunks_budget_one_returns_v_exactly():
         np.testing.assert_array_equal(got[:, h], x.v[0][:, h // 2])
 
 
-def test_empty_rows_give_zero_and_minus_inf():
+def test_empty_rows_give_zero_and_minus_inf(block_m):
     w = synth.small_workload("empty", 1, 512, 2, 1, (50, 90), "iid", topk=2, seed=41)
     x = synth.generate(w)
     offs = dhsa.ChunkOffsets.from_list(x.offsets, w.seq_len)
@@ -315,7 +322,7 @@ def test_custom_scale_matches_oracle():
     assert_attention_close(orc.widen_bf16(to_np_bf16(out))[0], O_ref, "scale 0.05")
 
 
-def test_outputs_are_deterministic():
+def test_outputs_are_deterministic(block_m):
     c = get_case("mid_ragged")
     a = dhsa.build_mask(c.q, c.k, c.offs, c.topk)
     oa = dhsa.sparse_prefill(c.q, c.k, c.v, c.offs, a).clone()
