@@ -337,11 +337,11 @@ int dhsa_build_mask(const void* q, const void* k, int32_t batch, int32_t seq_len
                              static_cast<const uint16_t*>(k), kbar, num_kv_heads, (int32_t)tc,
                              chunk_offsets_dev, st, seq_len, strm);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
+  const int cmax = max_chunks(batch, num_chunks);
   e = launch_scores(qbar, kbar, scores, num_q_heads, num_kv_heads, st,
                     score_tiles(batch, num_chunks, num_q_heads), strm);
   if (e != hipSuccess) return hip_fail(e, "chunk score launch");
-  e = launch_topk(scores, st, num_q_heads, R, topk, max_chunks(batch, num_chunks), row_ptr,
-                  col_idx, strm);
+  e = launch_topk(scores, st, num_q_heads, R, topk, cmax, row_ptr, col_idx, strm);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
 }

@@ -7,12 +7,10 @@
 // order, so scores are reproducible run to run.  The contraction index is
 // split by lane half: lanes 0-31 feed d in [0,64), lanes 32-63 feed d in
 // [64,128), so each lane streams one contiguous 256-byte half row.
-#include "dhsa_internal.h"
+#include "score_tile.h"
 
 namespace dhsa {
 namespace {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct ScoreGrid {
   int32_t stbase[kMaxBatch + 1];  // first tile of each sequence
@@ -45,25 +43,10 @@ __global__ __launch_bounds__(64) void scores_kernel(const float* __restrict__ qb
   const float* qp = qbar + ((size_t)hq * st.cbase[b] + (size_t)h * C + (i0 + row)) * kHeadDim + 64 * half;
   const float* kp = kbar + ((size_t)hkv * st.cbase[b] + (size_t)(h / G) * C + (j0 + row)) * kHeadDim + 64 * half;
 
-  f32x16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int part = 0; part < 4; ++part) {
-    float4 qv[4], kv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      qv[u] = qok ? reinterpret_cast<const float4*>(qp)[part * 4 + u] : make_float4(0, 0, 0, 0);
-      kv[u] = kok ? reinterpret_cast<const float4*>(kp)[part * 4 + u] : make_float4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[u].x, kv[u].x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[u].y, kv[u].y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[u].z, kv[u].z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[u].w, kv[u].w, acc, 0, 0, 0);
-    }
-  }
+  float4 qv[16], kv[16];
+  load_half_row(qp, qok, qv);
+  load_half_row(kp, kok, kv);
+  const f32x16_t acc = score_tile(qv, kv);
   // accumulator layout: lane -> column j0 + (lane & 31); register r -> row
   // i0 + 8*(r/4) + 4*(lane/32) + r%4
   float* sp = scores + st.sbase[b] + (size_t)h * C * C;

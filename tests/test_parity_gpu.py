@@ -51,6 +51,9 @@ CASES = {
     # rows with more kept chunks than one LDS table window (512)
     "many_entries": synth.small_workload("many_entries", 1, 4096, 2, 1, (4, 10), "iid",
                                          topk=100000, seed=36),
+    # more than 1024 chunks per sequence (17 candidate slots per lane)
+    "many_chunks": synth.small_workload("many_chunks", 1, 4096, 2, 1, (1, 4), "iid", topk=8,
+                                        seed=37),
 }
 
 _cache = {}
@@ -147,7 +150,8 @@ def test_pool_parity(name):
             assert np.all(err <= bound + 1e-30), (which, b, err.max())
 
 
-@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "many_entries"])
+@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "many_entries",
+                                  "many_chunks"])
 def test_chunk_score_parity(name):
     c = get_case(name)
     say("  build_mask with scores")
@@ -182,6 +186,26 @@ def test_topk_bit_exact_on_oracle_scores(name):
     np.testing.assert_array_equal(ci, c.ci)
 
 
+@pytest.mark.parametrize("name", ["mid_ragged", "mid_structured"])
+def test_build_mask_equals_stage_kernels(name):
+    # dhsa_build_mask and the stage calls (pool, chunk scores, top-k) run the
+    # same kernels: scores and masks must agree bit for bit
+    c = get_case(name)
+    csr, flat = dhsa.build_mask(c.q, c.k, c.offs, c.topk, return_scores=True)
+    qbar = dhsa.pool(c.q, c.offs)
+    kbar = dhsa.pool(c.k, c.offs)
+    flat2 = dhsa.chunk_scores(qbar, kbar, c.offs, c.hq, c.hkv)
+    csr2 = dhsa.topk_csr(flat2, c.offs, c.hq, c.topk)
+    torch.cuda.synchronize()
+    per1 = split_scores(flat.cpu().numpy(), c)
+    per2 = split_scores(flat2.cpu().numpy(), c)
+    for a, b2 in zip(per1, per2):
+        low = np.tril(np.ones(a.shape[1:], dtype=bool))
+        np.testing.assert_array_equal(a[:, low].view(np.uint32), b2[:, low].view(np.uint32))
+    assert torch.equal(csr.row_ptr, csr2.row_ptr)
+    assert torch.equal(csr.col_idx[:csr.nnz], csr2.col_idx[:csr2.nnz])
+
+
 def test_topk_ties_and_signed_zero():
     # hand-built rows with exact ties and -0/+0: lowest index must win
     C, hq, k = 70, 1, 4
@@ -201,7 +225,8 @@ def test_topk_ties_and_signed_zero():
     assert ref_rows[0][69] == [0, 1, 2, 69]
 
 
-@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "topk1"])
+@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "topk1",
+                                  "many_chunks"])
 def test_build_mask_matches_oracle_mask(name):
     c = get_case(name)
     csr = dhsa.build_mask(c.q, c.k, c.offs, c.topk)
