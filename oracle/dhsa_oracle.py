@@ -155,10 +155,44 @@ def select_row(scores_row: np.ndarray, i: int, k: int) -> List[int]:
     return keep + [i]
 
 
+def select_row_ex(scores_row: np.ndarray, i: int, budget: int, recent: int) -> List[int]:
+    """Kept chunks of query chunk i with a row budget and a recent window.
+
+    The row keeps chunk i, the `recent` chunks just before it and the
+    budget - 1 best-scoring chunks among the older ones (j < i - recent),
+    under the same order as select_row; when i + 1 <= budget + recent it
+    keeps every chunk 0..i.  Readings of the pages: the README's dynamic
+    predictors use query-dependent row budgets ("Predictor Checkpoints"), and
+    the codewithpapers record names a recent-key-block keep OR'ed with a
+    scattered top-k by row budget; the pages give no formula, so this is the
+    plainest rule consistent with both.  With recent = 0 it is select_row.
+    """
+    if budget < 1 or recent < 0:
+        raise ValueError("budget must be >= 1 and recent >= 0")
+    if i + 1 <= budget + recent:
+        return list(range(i + 1))
+    older = i - recent  # candidates j < older
+    cand = np.asarray(scores_row[:older], dtype=np.float64)
+    if not np.all(np.isfinite(cand)):
+        raise ValueError("scores must be finite")
+    j = np.arange(older)
+    order = np.lexsort((j, -cand))
+    keep = sorted(int(x) for x in order[:budget - 1])
+    return keep + list(range(older, i + 1))
+
+
 def select_topk(scores: np.ndarray, k: int) -> List[List[List[int]]]:
     """rows[h][i] for one sequence; scores [Hq, C, C] (lower triangle read)."""
     Hq, C, _ = scores.shape
     return [[select_row(scores[h, i], i, k) for i in range(C)] for h in range(Hq)]
+
+
+def select_topk_ex(scores: np.ndarray, budgets: np.ndarray, recent: int
+                   ) -> List[List[List[int]]]:
+    """rows[h][i] with a budget per row (budgets [Hq, C]) and a recent window."""
+    Hq, C, _ = scores.shape
+    return [[select_row_ex(scores[h, i], i, int(budgets[h, i]), recent) for i in range(C)]
+            for h in range(Hq)]
 
 
 def rows_to_csr(rows_per_seq: Sequence[Sequence[Sequence[Sequence[int]]]]

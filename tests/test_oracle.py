@@ -349,3 +349,48 @@ def test_oracle_selects_planted_needles():
     for (_b, i, j, g) in x.needles:
         for h in range(g * G, (g + 1) * G):
             assert j in rows[h][i], (i, j, h)
+
+
+# ---------------------------------------------------------------- budgets, recent window
+
+
+def test_budget_recent_worked_example():
+    g = _load("topk_budget_recent_worked_example.json")
+    S = np.array([[_parse(v) for v in row] for row in g["scores"]], dtype=np.float64)
+    got = [orc.select_row_ex(S[i], i, g["budgets"][i], g["recent"]) for i in range(S.shape[0])]
+    assert got == g["rows"], got
+
+
+def _brute_force_row_ex(s, i, budget, recent):
+    # independent rank count over the older candidates, then the window
+    if i + 1 <= budget + recent:
+        return list(range(i + 1))
+    older = i - recent
+    keep = []
+    for j in range(older):
+        better = sum(1 for jj in range(older) if s[jj] > s[j] or (s[jj] == s[j] and jj < j))
+        if better < budget - 1:
+            keep.append(j)
+    return keep + list(range(older, i + 1))
+
+
+def test_budget_recent_vs_brute_force_and_closed_forms():
+    rng = np.random.default_rng(14)
+    for _ in range(25):
+        C = int(rng.integers(1, 35))
+        S = rng.integers(-3, 4, size=(C, C)).astype(np.float32)
+        S[S == 0] = -0.0
+        recent = int(rng.integers(0, 6))
+        for i in range(C):
+            budget = int(rng.integers(1, 8))
+            got = orc.select_row_ex(S[i], i, budget, recent)
+            assert got == _brute_force_row_ex(S[i], i, budget, recent)
+            assert got[-1] == i and got == sorted(got) and len(got) == min(i + 1, budget + recent)
+            # the recent window is always kept
+            assert all(j in got for j in range(max(0, i - recent), i + 1))
+            if budget == 1:
+                assert got == list(range(max(0, i - recent), i + 1))
+        # recent = 0 with a fixed budget is the plain fixed-budget selection
+        k = int(rng.integers(1, 6))
+        assert [orc.select_row_ex(S[i], i, k, 0) for i in range(C)] == \
+            [_brute_force_row(S[i], i, k) for i in range(C)]
