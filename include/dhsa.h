@@ -13,7 +13,8 @@
  *   dhsa_build_mask     q, k, chunk offsets, top-k  ->  CSR block list
  *   dhsa_sparse_prefill q, k, v, CSR                ->  out (and optional LSE)
  * and three stage calls expose its steps one by one (pool, chunk scores,
- * top-k) for stage-wise checking.
+ * top-k) for stage-wise checking.  dhsa_build_mask_ex and dhsa_topk_csr_ex
+ * widen the selection rule with per-row budgets and a recent-chunk window.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -72,7 +73,7 @@ typedef enum dhsa_status {
   DHSA_ERR_NULL_POINTER = -1,   /* a required pointer is NULL               */
   DHSA_ERR_SHAPE = -2,          /* batch/heads/head_dim/seq_len not allowed */
   DHSA_ERR_OFFSETS = -3,        /* offsets not 0 < ... < L, or C_b invalid  */
-  DHSA_ERR_TOPK = -4,           /* topk < 1                                 */
+  DHSA_ERR_TOPK = -4,           /* topk < 1 or recent < 0                   */
   DHSA_ERR_CAPACITY = -5,       /* output or workspace buffer too small     */
   DHSA_ERR_CSR = -6,            /* CSR size arguments inconsistent          */
   DHSA_ERR_UNSUPPORTED = -7,    /* beyond a documented limit                */
@@ -98,6 +99,14 @@ int dhsa_version(void);
  * budget.)  num_chunks: host [batch].  Outputs may not be NULL. */
 int dhsa_csr_size(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
                   int32_t topk, int32_t* num_rows, int64_t* nnz);
+
+/* CSR sizes when each row keeps at most min(topk + recent, i + 1) chunks:
+ * nnz = Hq * sum_b sum_i min(topk + recent, i + 1).  Exact for one budget
+ * per layer (row_budgets NULL in the _ex calls); with per-row budgets (each
+ * capped at topk) it is the capacity col_idx needs, and the exact count is
+ * row_ptr[R] on the device.  recent >= 0; dhsa_csr_size is recent = 0. */
+int dhsa_csr_capacity(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
+                      int32_t topk, int32_t recent, int32_t* num_rows, int64_t* nnz);
 
 /* Bytes of device workspace dhsa_build_mask needs: pooled Q and K (fp32) and
  * the chunk-score matrices (fp32), each 256-byte aligned. */
@@ -144,6 +153,32 @@ int dhsa_build_mask(const void* q, const void* k,
                     int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                     float* scores_out, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* dhsa_build_mask with a wider selection rule (DHSA README, "Predictor
+ * Checkpoints": static predictors use a fixed row budget, dynamic ones a
+ * query-dependent budget per row; the codewithpapers record of the DHSA
+ * repository names a recent-key-block keep OR'ed with a scattered top-k by
+ * row budget, without a formula).  Row (b,h,i) with budget k_r keeps:
+ *   - chunk i and the `recent` chunks just before it (i-recent .. i-1),
+ *   - the k_r - 1 highest-scoring chunks among j < i - recent (order and
+ *     ties as in dhsa_build_mask),
+ *   - every chunk 0..i when i + 1 <= k_r + recent.
+ * row_budgets: NULL -> k_r = topk for every row; else device int32 [R] in
+ *   CSR row order, read on the device, each value clamped to [1, topk]
+ *   (so a predictor's output needs no host round trip), and row_ptr is
+ *   built by a device prefix sum.
+ * recent >= 0 (0 with NULL budgets is exactly dhsa_build_mask).
+ * col_capacity >= nnz of dhsa_csr_capacity(topk, recent).  Other arguments,
+ * outputs and errors as dhsa_build_mask. */
+int dhsa_build_mask_ex(const void* q, const void* k,
+                       int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim,
+                       const int32_t* num_chunks, const int32_t* chunk_offsets,
+                       const int32_t* chunk_offsets_dev, int32_t topk,
+                       const int32_t* row_budgets, int32_t recent,
+                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                       float* scores_out, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* Block-sparse causal attention forward over the kept chunk tiles.
  * For query token t of chunk i, head h: out = softmax(scale * q_t k_s^T) v_s
@@ -198,6 +233,14 @@ int dhsa_chunk_scores(const float* qbar, const float* kbar, int32_t batch,
 int dhsa_topk_csr(const float* scores, int32_t batch, int32_t num_q_heads,
                   const int32_t* num_chunks, int32_t topk, int32_t* row_ptr,
                   int32_t* col_idx, int64_t col_capacity, void* stream);
+
+/* dhsa_topk_csr with the selection rule of dhsa_build_mask_ex (row_budgets
+ * nullable device int32 [R], clamped to [1, topk]; recent >= 0;
+ * col_capacity >= nnz of dhsa_csr_capacity). */
+int dhsa_topk_csr_ex(const float* scores, int32_t batch, int32_t num_q_heads,
+                     const int32_t* num_chunks, int32_t topk,
+                     const int32_t* row_budgets, int32_t recent, int32_t* row_ptr,
+                     int32_t* col_idx, int64_t col_capacity, void* stream);
 
 #ifdef __cplusplus
 }

@@ -80,8 +80,10 @@ int64_t entries_per_head(int64_t C, int64_t k) {
   return C <= k ? C * (C + 1) / 2 : k * (k + 1) / 2 + (C - k) * k;
 }
 
+// per_row: entries a row i keeps at most (budget + recent window), 0 when the
+// table is not used for CSR offsets
 void fill_table(SeqTable& st, int32_t batch, const int32_t* num_chunks, int32_t hq,
-                int32_t topk) {
+                int64_t per_row) {
   memset(&st, 0, sizeof(st));
   st.batch = batch;
   int64_t cb = 0, sb = 0, nb = 0;
@@ -93,7 +95,7 @@ void fill_table(SeqTable& st, int32_t batch, const int32_t* num_chunks, int32_t 
     st.nbase[b] = nb;
     cb += C;
     sb += (int64_t)hq * C * C;
-    if (topk > 0) nb += (int64_t)hq * entries_per_head(C, topk);
+    if (per_row > 0) nb += (int64_t)hq * entries_per_head(C, per_row);
   }
 }
 
@@ -184,25 +186,32 @@ const char* dhsa_status_string(int status) {
 
 const char* dhsa_last_error(void) { return g_err; }
 
-int dhsa_version(void) { return 100; }
+int dhsa_version(void) { return 101; }
 
-int dhsa_csr_size(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads, int32_t topk,
-                  int32_t* num_rows, int64_t* nnz) {
+int dhsa_csr_capacity(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
+                      int32_t topk, int32_t recent, int32_t* num_rows, int64_t* nnz) {
   if (num_rows == nullptr || nnz == nullptr) return fail(DHSA_ERR_NULL_POINTER, "output pointer is NULL");
   int s = check_batch_chunks(batch, num_chunks);
   if (s) return s;
   if (num_q_heads < 1) return fail(DHSA_ERR_SHAPE, "num_q_heads %d < 1", num_q_heads);
   if (topk < 1) return fail(DHSA_ERR_TOPK, "topk %d < 1", topk);
+  if (recent < 0) return fail(DHSA_ERR_TOPK, "recent %d < 0", recent);
+  const int64_t m = (int64_t)topk + recent;
   int64_t R = 0, N = 0;
   for (int b = 0; b < batch; ++b) {
     R += (int64_t)num_q_heads * num_chunks[b];
-    N += (int64_t)num_q_heads * entries_per_head(num_chunks[b], topk);
+    N += (int64_t)num_q_heads * entries_per_head(num_chunks[b], m);
   }
   if (R > INT32_MAX - 1 || N > INT32_MAX)
     return fail(DHSA_ERR_UNSUPPORTED, "CSR too large for int32 indices");
   *num_rows = (int32_t)R;
   *nnz = N;
   return ok();
+}
+
+int dhsa_csr_size(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads, int32_t topk,
+                  int32_t* num_rows, int64_t* nnz) {
+  return dhsa_csr_capacity(batch, num_chunks, num_q_heads, topk, 0, num_rows, nnz);
 }
 
 int dhsa_mask_workspace_size(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
@@ -270,33 +279,47 @@ int dhsa_chunk_scores(const float* qbar, const float* kbar, int32_t batch, int32
   return ok();
 }
 
-int dhsa_topk_csr(const float* scores, int32_t batch, int32_t num_q_heads,
-                  const int32_t* num_chunks, int32_t topk, int32_t* row_ptr, int32_t* col_idx,
-                  int64_t col_capacity, void* stream) {
+int dhsa_topk_csr_ex(const float* scores, int32_t batch, int32_t num_q_heads,
+                     const int32_t* num_chunks, int32_t topk, const int32_t* row_budgets,
+                     int32_t recent, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                     void* stream) {
   if (!scores || !row_ptr || !col_idx) return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
   int32_t R;
   int64_t nnz;
-  int s = dhsa_csr_size(batch, num_chunks, num_q_heads, topk, &R, &nnz);
+  int s = dhsa_csr_capacity(batch, num_chunks, num_q_heads, topk, recent, &R, &nnz);
   if (s) return s;
-  if (max_chunks(batch, num_chunks) > kMaxChunks)
+  const int cmax = max_chunks(batch, num_chunks);
+  if (cmax > kMaxChunks)
     return fail(DHSA_ERR_UNSUPPORTED, "more than %d chunks in a sequence", kMaxChunks);
   if (col_capacity < nnz)
     return fail(DHSA_ERR_CAPACITY, "col_capacity %lld < nnz %lld", (long long)col_capacity,
                 (long long)nnz);
+  // a budget or window beyond the longest sequence keeps the same chunks as
+  // one equal to it, so both are clamped there (keeps device sums in int32)
+  const int32_t k_dev = topk < cmax ? topk : cmax;
+  const int32_t w_dev = recent < cmax ? recent : cmax;
   SeqTable st;
-  fill_table(st, batch, num_chunks, num_q_heads, topk);
-  hipError_t e = launch_topk(scores, st, num_q_heads, R, topk, max_chunks(batch, num_chunks),
+  fill_table(st, batch, num_chunks, num_q_heads, (int64_t)k_dev + w_dev);
+  hipError_t e = launch_topk(scores, st, num_q_heads, R, k_dev, w_dev, row_budgets, cmax,
                              row_ptr, col_idx, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
 }
 
-int dhsa_build_mask(const void* q, const void* k, int32_t batch, int32_t seq_len,
-                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                    const int32_t* num_chunks, const int32_t* chunk_offsets,
-                    const int32_t* chunk_offsets_dev, int32_t topk, int32_t* row_ptr,
-                    int32_t* col_idx, int64_t col_capacity, float* scores_out, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int dhsa_topk_csr(const float* scores, int32_t batch, int32_t num_q_heads,
+                  const int32_t* num_chunks, int32_t topk, int32_t* row_ptr, int32_t* col_idx,
+                  int64_t col_capacity, void* stream) {
+  return dhsa_topk_csr_ex(scores, batch, num_q_heads, num_chunks, topk, nullptr, 0, row_ptr,
+                          col_idx, col_capacity, stream);
+}
+
+int dhsa_build_mask_ex(const void* q, const void* k, int32_t batch, int32_t seq_len,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       const int32_t* num_chunks, const int32_t* chunk_offsets,
+                       const int32_t* chunk_offsets_dev, int32_t topk,
+                       const int32_t* row_budgets, int32_t recent, int32_t* row_ptr,
+                       int32_t* col_idx, int64_t col_capacity, float* scores_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !chunk_offsets_dev || !row_ptr || !col_idx || !workspace)
     return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
   int s = check_batch_chunks(batch, num_chunks);
@@ -307,9 +330,10 @@ int dhsa_build_mask(const void* q, const void* k, int32_t batch, int32_t seq_len
   if (s) return s;
   int32_t R;
   int64_t nnz;
-  s = dhsa_csr_size(batch, num_chunks, num_q_heads, topk, &R, &nnz);
+  s = dhsa_csr_capacity(batch, num_chunks, num_q_heads, topk, recent, &R, &nnz);
   if (s) return s;
-  if (max_chunks(batch, num_chunks) > kMaxChunks)
+  const int cmax = max_chunks(batch, num_chunks);
+  if (cmax > kMaxChunks)
     return fail(DHSA_ERR_UNSUPPORTED, "more than %d chunks in a sequence", kMaxChunks);
   if (col_capacity < nnz)
     return fail(DHSA_ERR_CAPACITY, "col_capacity %lld < nnz %lld", (long long)col_capacity,
@@ -330,20 +354,34 @@ int dhsa_build_mask(const void* q, const void* k, int32_t batch, int32_t seq_len
   ws += align_up((size_t)num_kv_heads * tc * kHeadDim * sizeof(float));
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
 
+  const int32_t k_dev = topk < cmax ? topk : cmax;
+  const int32_t w_dev = recent < cmax ? recent : cmax;
   SeqTable st;
-  fill_table(st, batch, num_chunks, num_q_heads, topk);
+  fill_table(st, batch, num_chunks, num_q_heads, (int64_t)k_dev + w_dev);
   hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e = launch_pool(static_cast<const uint16_t*>(q), qbar, num_q_heads,
                              static_cast<const uint16_t*>(k), kbar, num_kv_heads, (int32_t)tc,
                              chunk_offsets_dev, st, seq_len, strm);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
-  const int cmax = max_chunks(batch, num_chunks);
   e = launch_scores(qbar, kbar, scores, num_q_heads, num_kv_heads, st,
                     score_tiles(batch, num_chunks, num_q_heads), strm);
   if (e != hipSuccess) return hip_fail(e, "chunk score launch");
-  e = launch_topk(scores, st, num_q_heads, R, topk, cmax, row_ptr, col_idx, strm);
+  e = launch_topk(scores, st, num_q_heads, R, k_dev, w_dev, row_budgets, cmax, row_ptr, col_idx,
+                  strm);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
+}
+
+int dhsa_build_mask(const void* q, const void* k, int32_t batch, int32_t seq_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    const int32_t* num_chunks, const int32_t* chunk_offsets,
+                    const int32_t* chunk_offsets_dev, int32_t topk, int32_t* row_ptr,
+                    int32_t* col_idx, int64_t col_capacity, float* scores_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return dhsa_build_mask_ex(q, k, batch, seq_len, num_q_heads, num_kv_heads, head_dim,
+                            num_chunks, chunk_offsets, chunk_offsets_dev, topk, nullptr, 0,
+                            row_ptr, col_idx, col_capacity, scores_out, workspace,
+                            workspace_bytes, stream);
 }
 
 int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t batch,

@@ -51,9 +51,12 @@ hipError_t launch_scores(const float* qbar, const float* kbar, float* scores,
                          int32_t hq, int32_t hkv, const SeqTable& st,
                          int64_t total_tiles, hipStream_t stream);
 
+// topk: the uniform row budget, or the cap of the per-row budgets when
+// budgets (device int32, one per CSR row) is not NULL; recent: window width.
 hipError_t launch_topk(const float* scores, const SeqTable& st, int32_t hq,
-                       int32_t total_rows, int32_t topk, int32_t max_chunks,
-                       int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
+                       int32_t total_rows, int32_t topk, int32_t recent,
+                       const int32_t* budgets, int32_t max_chunks, int32_t* row_ptr,
+                       int32_t* col_idx, hipStream_t stream);
 
 hipError_t launch_plan_tiles(const int32_t* offs_dev, const SeqTable& st,
                              int4* tiles, int32_t block_m, hipStream_t stream);

@@ -1,21 +1,24 @@
-// Per-row causal top-k selection (device side), shared by the stand-alone
-// top-k kernel and the fused score + top-k kernel.
+// Per-row causal chunk selection (device side) for the top-k kernel.
 //
-// Row (b,h,i) keeps its diagonal chunk i plus the topk-1 earlier chunks with
-// the highest scores; when i + 1 <= topk it keeps every chunk 0..i
-// (gist.science Technical Summary, Methodology, Step 2: each query chunk is
-// routed to its highest-scoring chunks under the causal constraint; DHSA
-// README, "Predictor Checkpoints": a fixed row budget).  The order is total:
+// Row (b,h,i) with budget k and recent window w keeps chunk i, the w chunks
+// just before it, and the k-1 highest-scoring chunks among the older ones
+// (j < i - w); when i + 1 <= k + w it keeps every chunk 0..i.  With w = 0
+// this is the fixed-budget rule: the diagonal plus the k-1 best earlier
+// chunks (gist.science Technical Summary, Methodology, Step 2: each query
+// chunk is routed to its highest-scoring chunks under the causal constraint;
+// DHSA README, "Predictor Checkpoints": fixed and query-dependent row
+// budgets; the codewithpapers record of the repository names a recent-block
+// keep OR'ed with a scattered top-k by row budget).  The order is total:
 // score descending, then chunk index ascending; -0 and +0 are equal; NaN
 // ranks below every number.
 //
-// One wavefront owns one row.  Candidate j < i sits in lane j % 64, slot
-// j / 64, as an order-preserving 32-bit key of its score.  Each of the
-// topk-1 rounds takes every lane's best untaken candidate, reduces the keys
-// across the wave with DPP moves, and picks the holder of the maximum (the
-// lowest chunk index when several lanes hold it).  The winners are emitted in
-// ascending index order by a ballot and prefix popcount per slot, and the
-// diagonal goes last.
+// One wavefront owns one row.  Candidate j sits in lane j % 64, slot j / 64,
+// as an order-preserving 32-bit key of its score.  Each of the k-1 rounds
+// takes every lane's best untaken candidate, reduces the keys across the
+// wave with DPP moves, and picks the holder of the maximum (the lowest chunk
+// index when several lanes hold it).  The winners are emitted in ascending
+// index order by a ballot and prefix popcount per slot; the window chunks
+// i-w..i follow them.
 #pragma once
 
 #include "dhsa_internal.h"
@@ -29,7 +32,8 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// entries in rows 0..i-1 of one head: sum_{i' < i} min(k, i'+1)
+// entries in rows 0..i-1 of one head when every row keeps min(k, i'+1):
+// sum_{i' < i} min(k, i'+1)  (k = budget + recent window)
 __device__ __forceinline__ int64_t entries_before(int64_t i, int64_t k) {
   return i <= k ? i * (i + 1) / 2 : k * (k + 1) / 2 + (i - k) * k;
 }
@@ -71,24 +75,25 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Writes the kept chunks of row i (ascending) to out[0 .. min(k, i+1)-1];
-// srow[j] is the score of key chunk j (j < i are read).  All 64 lanes of
-// the wave call it together.
+// Writes the kept chunks of row i (ascending) to out[0 .. min(k+w, i+1)-1];
+// srow[j] is the score of key chunk j (j < i - w are read).  All 64 lanes
+// of the wave call it together; k >= 1, w >= 0.
 template <int NS>
-__device__ __forceinline__ void select_row(const float* srow, int i, int64_t k, int lane,
+__device__ __forceinline__ void select_row(const float* srow, int i, int k, int w, int lane,
                                            int32_t* out) {
-  if (i + 1 <= k) {
+  if (i + 1 <= k + w) {
     for (int j = lane; j <= i; j += 64) out[j] = j;
     return;
   }
+  const int older = i - w;  // candidates j < older; older >= k >= 1
   uint32_t key[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int j = lane + 64 * s;
-    key[s] = j < i ? order_key(srow[j]) : 0u;  // 0: empty slot
+    key[s] = j < older ? order_key(srow[j]) : 0u;  // 0: empty slot
   }
   uint32_t taken = 0;
-  for (int round = 0; round < (int)k - 1; ++round) {
+  for (int round = 0; round < k - 1; ++round) {
     // this lane's best untaken candidate (the lowest slot among equal keys)
     uint32_t best = 0;
     int bslot = 0;
@@ -123,7 +128,8 @@ __device__ __forceinline__ void select_row(const float* srow, int i, int64_t k, 
     }
     base += __popcll(m);
   }
-  if (lane == 0) out[k - 1] = i;
+  // the recent window and the diagonal: chunks older..i
+  for (int t = lane; t <= w; t += 64) out[k - 1 + t] = older + t;
 }
 
 }  // namespace dhsa

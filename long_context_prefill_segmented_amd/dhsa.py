@@ -45,16 +45,22 @@ _SIGNATURES = {
     "dhsa_last_error": (ctypes.c_char_p, []),
     "dhsa_version": (ctypes.c_int, []),
     "dhsa_csr_size": (ctypes.c_int, [_i32, _vp, _i32, _i32, _pi32, _pi64]),
+    "dhsa_csr_capacity": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _pi32, _pi64]),
     "dhsa_mask_workspace_size": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _psz]),
     "dhsa_prefill_workspace_size": (ctypes.c_int, [_i32, _i32, _vp, _vp, _psz]),
     "dhsa_build_mask": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                        _i32, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "dhsa_build_mask_ex": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                          _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _sz,
+                                          _vp]),
     "dhsa_sparse_prefill": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                            _vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp, _vp, _sz,
                                            _vp]),
     "dhsa_pool": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "dhsa_chunk_scores": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "dhsa_topk_csr": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _i64, _vp]),
+    "dhsa_topk_csr_ex": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64,
+                                        _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -143,6 +149,25 @@ def csr_size(offsets: ChunkOffsets, num_q_heads: int, topk: int):
     return R.value, nnz.value
 
 
+def csr_capacity(offsets: ChunkOffsets, num_q_heads: int, topk: int, recent: int = 0):
+    """(R, nnz bound) when rows keep at most min(topk + recent, i + 1) chunks."""
+    R = _i32()
+    nnz = _i64()
+    check(lib.dhsa_csr_capacity(offsets.batch, _np_ptr(offsets.num_chunks), num_q_heads, topk,
+                                recent, ctypes.byref(R), ctypes.byref(nnz)))
+    return R.value, nnz.value
+
+
+def _budgets_ptr(row_budgets, num_rows: int):
+    if row_budgets is None:
+        return None
+    torch = _torch()
+    if (row_budgets.dtype != torch.int32 or not row_budgets.is_contiguous()
+            or not row_budgets.is_cuda or row_budgets.numel() != num_rows):
+        raise ValueError(f"row_budgets must be a contiguous CUDA int32 tensor of {num_rows} rows")
+    return _dptr(row_budgets)
+
+
 def mask_workspace_size(offsets: ChunkOffsets, hq: int, hkv: int) -> int:
     n = _sz()
     check(lib.dhsa_mask_workspace_size(offsets.batch, _np_ptr(offsets.num_chunks), hq, hkv,
@@ -177,38 +202,53 @@ def scores_numel(offsets: ChunkOffsets, num_q_heads: int) -> int:
 
 
 class MaskBuilder:
-    """Preallocated buffers for repeated dhsa_build_mask calls on one shape."""
+    """Preallocated buffers for repeated mask builds on one shape.
+
+    topk is the row budget (the cap of per-row budgets when row_budgets is
+    given to a call); recent is the window of chunks before the diagonal
+    that every row keeps.  With recent = 0 and no row budgets this is
+    dhsa_build_mask, otherwise dhsa_build_mask_ex.  csr.nnz is the col_idx
+    capacity (exact for a single budget; row_ptr[-1] is the exact count)."""
 
     def __init__(self, offsets: ChunkOffsets, hq: int, hkv: int, topk: int, device="cuda",
-                 keep_scores: bool = False):
+                 keep_scores: bool = False, recent: int = 0):
         torch = _torch()
-        self.offsets, self.hq, self.hkv, self.topk = offsets, hq, hkv, topk
-        R, nnz = csr_size(offsets, hq, topk)
+        self.offsets, self.hq, self.hkv, self.topk, self.recent = offsets, hq, hkv, topk, recent
+        R, nnz = csr_capacity(offsets, hq, topk, recent)
         self.csr = CSR(torch.empty(R + 1, dtype=torch.int32, device=device),
                        torch.empty(max(nnz, 1), dtype=torch.int32, device=device), nnz)
         self.ws = _workspace(mask_workspace_size(offsets, hq, hkv), device)
         self.scores = (torch.empty(scores_numel(offsets, hq), dtype=torch.float32, device=device)
                        if keep_scores else None)
 
-    def __call__(self, q, k, stream=None) -> CSR:
+    def __call__(self, q, k, stream=None, row_budgets=None) -> CSR:
         o = self.offsets
-        check(lib.dhsa_build_mask(
-            _dptr(q), _dptr(k), o.batch, o.seq_len, self.hq, self.hkv, HEAD_DIM,
-            _np_ptr(o.num_chunks), _np_ptr(o.host), _dptr(o.device), self.topk,
-            _dptr(self.csr.row_ptr), _dptr(self.csr.col_idx), self.csr.col_idx.numel(),
-            _dptr(self.scores) if self.scores is not None else None,
-            _dptr(self.ws), self.ws.numel(), _stream_ptr(stream)))
+        scores = _dptr(self.scores) if self.scores is not None else None
+        if row_budgets is None and self.recent == 0:
+            check(lib.dhsa_build_mask(
+                _dptr(q), _dptr(k), o.batch, o.seq_len, self.hq, self.hkv, HEAD_DIM,
+                _np_ptr(o.num_chunks), _np_ptr(o.host), _dptr(o.device), self.topk,
+                _dptr(self.csr.row_ptr), _dptr(self.csr.col_idx), self.csr.col_idx.numel(),
+                scores, _dptr(self.ws), self.ws.numel(), _stream_ptr(stream)))
+        else:
+            check(lib.dhsa_build_mask_ex(
+                _dptr(q), _dptr(k), o.batch, o.seq_len, self.hq, self.hkv, HEAD_DIM,
+                _np_ptr(o.num_chunks), _np_ptr(o.host), _dptr(o.device), self.topk,
+                _budgets_ptr(row_budgets, self.csr.num_rows), self.recent,
+                _dptr(self.csr.row_ptr), _dptr(self.csr.col_idx), self.csr.col_idx.numel(),
+                scores, _dptr(self.ws), self.ws.numel(), _stream_ptr(stream)))
         return self.csr
 
 
 def build_mask(q, k, offsets: ChunkOffsets, topk: int, return_scores: bool = False,
-               stream=None):
-    """dhsa_build_mask: pooled chunk scores -> causal top-k CSR block list."""
+               stream=None, row_budgets=None, recent: int = 0):
+    """dhsa_build_mask(_ex): pooled chunk scores -> causal chunk selection as CSR."""
     _check_qkv(q, k)
     B, L, hq, _ = q.shape
     hkv = k.shape[2]
-    mb = MaskBuilder(offsets, hq, hkv, topk, device=q.device, keep_scores=return_scores)
-    csr = mb(q, k, stream)
+    mb = MaskBuilder(offsets, hq, hkv, topk, device=q.device, keep_scores=return_scores,
+                     recent=recent)
+    csr = mb(q, k, stream, row_budgets=row_budgets)
     return (csr, mb.scores) if return_scores else csr
 
 
@@ -268,17 +308,24 @@ def chunk_scores(qbar, kbar, offsets: ChunkOffsets, hq: int, hkv: int, stream=No
     return out
 
 
-def topk_csr(scores, offsets: ChunkOffsets, hq: int, topk: int, stream=None) -> CSR:
-    """dhsa_topk_csr: CSR from given fp32 chunk scores."""
+def topk_csr(scores, offsets: ChunkOffsets, hq: int, topk: int, stream=None,
+             row_budgets=None, recent: int = 0) -> CSR:
+    """dhsa_topk_csr(_ex): CSR from given fp32 chunk scores."""
     torch = _torch()
     if scores.dtype != torch.float32 or not scores.is_contiguous():
         raise ValueError("scores must be contiguous float32")
-    R, nnz = csr_size(offsets, hq, topk)
+    R, nnz = csr_capacity(offsets, hq, topk, recent)
     csr = CSR(torch.empty(R + 1, dtype=torch.int32, device=scores.device),
               torch.empty(max(nnz, 1), dtype=torch.int32, device=scores.device), nnz)
-    check(lib.dhsa_topk_csr(_dptr(scores), offsets.batch, hq, _np_ptr(offsets.num_chunks), topk,
-                            _dptr(csr.row_ptr), _dptr(csr.col_idx), csr.col_idx.numel(),
-                            _stream_ptr(stream)))
+    if row_budgets is None and recent == 0:
+        check(lib.dhsa_topk_csr(_dptr(scores), offsets.batch, hq, _np_ptr(offsets.num_chunks),
+                                topk, _dptr(csr.row_ptr), _dptr(csr.col_idx),
+                                csr.col_idx.numel(), _stream_ptr(stream)))
+    else:
+        check(lib.dhsa_topk_csr_ex(_dptr(scores), offsets.batch, hq, _np_ptr(offsets.num_chunks),
+                                   topk, _budgets_ptr(row_budgets, R), recent,
+                                   _dptr(csr.row_ptr), _dptr(csr.col_idx), csr.col_idx.numel(),
+                                   _stream_ptr(stream)))
     return csr
 
 

@@ -271,3 +271,16 @@ def small_workload(name: str, batch: int, seq_len: int, hq: int, hkv: int,
         law = ((1.0, law[0], law[1]),)
     return Workload(name, batch, seq_len, hq, hkv, tuple(law), structure,
                     topk=topk, needles=needles, seed=seed)
+
+
+def row_budgets(num_chunks: Sequence[int], hq: int, topk: int, seed: int,
+                lo: int = 1, hi: Optional[int] = None) -> np.ndarray:
+    """Synthetic query-dependent row budgets, one per CSR row (sequence b,
+    query head h, query chunk i in that order), drawn uniformly from
+    [lo, hi] (default [1, 2 * topk - 1], mean topk).  They stand in for the
+    output of a trained budget predictor, whose weights are not available."""
+    if hi is None:
+        hi = 2 * topk - 1
+    rng = np.random.Generator(np.random.PCG64([seed, 0xB0D6]))
+    total = int(hq * sum(int(c) for c in num_chunks))
+    return rng.integers(lo, hi + 1, size=total, dtype=np.int64).astype(np.int32)

@@ -168,3 +168,46 @@ def test_stage_calls_reject_bad_arguments():
     assert lib.dhsa_chunk_scores(FAKE, FAKE, 1, 4, 3, 128, nc.ctypes.data, FAKE, None) == ESHAPE
     assert lib.dhsa_topk_csr(FAKE, 1, 4, nc.ctypes.data, 0, FAKE, FAKE, 100, None) == ETOPK
     assert lib.dhsa_topk_csr(FAKE, 1, 4, nc.ctypes.data, 2, FAKE, FAKE, 1, None) == ECAP
+
+
+def test_csr_capacity_closed_form():
+    # rows keep at most min(topk + recent, i + 1) chunks
+    for nc, hq, k, w in (([26], 2, 4, 0), ([26], 2, 4, 3), ([438], 32, 11, 2), ([5, 1, 9], 3, 2, 100)):
+        R = ctypes.c_int32()
+        N = ctypes.c_int64()
+        a = _arr(nc)
+        assert lib.dhsa_csr_capacity(a.size, a.ctypes.data, hq, k, w, ctypes.byref(R),
+                                     ctypes.byref(N)) == OK
+        assert R.value == hq * sum(nc)
+        assert N.value == hq * sum(sum(min(k + w, i + 1) for i in range(c)) for c in nc)
+        if w == 0:
+            assert (OK, R.value, N.value) == _csr_size(nc, hq, k)
+    a = _arr([10])
+    assert lib.dhsa_csr_capacity(1, a.ctypes.data, 2, 3, -1, ctypes.byref(ctypes.c_int32()),
+                                 ctypes.byref(ctypes.c_int64())) == ETOPK
+
+
+@cpu_only
+def test_ex_calls_reject_bad_arguments():
+    nc = _arr([3])
+    offs = _arr([0, 10, 50, 100])
+    # recent < 0, topk < 1, capacity below the topk + recent bound
+    assert lib.dhsa_topk_csr_ex(FAKE, 1, 4, nc.ctypes.data, 2, None, -1, FAKE, FAKE, 100,
+                                None) == ETOPK
+    assert lib.dhsa_topk_csr_ex(FAKE, 1, 4, nc.ctypes.data, 0, FAKE, 0, FAKE, FAKE, 100,
+                                None) == ETOPK
+    # topk 1 + recent 1: nnz = 4 * (1 + 2 + 2) = 20
+    assert lib.dhsa_topk_csr_ex(FAKE, 1, 4, nc.ctypes.data, 1, FAKE, 1, FAKE, FAKE, 19,
+                                None) == ECAP
+
+    def bm(**kw):
+        a = dict(topk=2, budgets=None, recent=0, cap=1 << 20, q=FAKE)
+        a.update(kw)
+        return lib.dhsa_build_mask_ex(a["q"], FAKE, 1, 100, 4, 2, 128, nc.ctypes.data,
+                                      offs.ctypes.data, FAKE, a["topk"], a["budgets"],
+                                      a["recent"], FAKE, FAKE, a["cap"], None, FAKE, 1 << 30,
+                                      None)
+    assert bm(q=None) == ENULL
+    assert bm(recent=-2) == ETOPK
+    assert bm(topk=0, budgets=FAKE) == ETOPK
+    assert bm(topk=2, recent=1, cap=23) == ECAP             # nnz bound = 4 * (1 + 2 + 3) = 24

@@ -1,0 +1,202 @@
+"""GPU parity of the widened selection rule (per-row budgets, recent-chunk
+window) through dhsa_topk_csr_ex / dhsa_build_mask_ex, against the oracle's
+select_topk_ex on the same seeded inputs.
+
+Bars as for the fixed budget: CSR bit-exact when the GPU selection consumes
+the oracle's fp32 scores; the whole-path mask equal to the oracle's except at
+near-ties within the score tolerance; attention |gpu - ref| <= 1e-2 +
+1e-2 |ref| on the resulting mask.  Budgets outside [1, topk] are clamped by
+the library (documented behaviour), so the oracle receives the clamped
+values."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from long_context_prefill_segmented_amd import dhsa, synth  # noqa: E402
+from oracle import dhsa_oracle as orc  # noqa: E402
+
+ATOL = RTOL = 1e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_np_bf16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+CASES = {
+    "tiny_1k": synth.WORKLOADS["tiny_1k"],
+    "mid_ragged": synth.small_workload("mid_ragged", 2, 4096, 8, 2,
+                                       ((0.70, 8, 32), (0.25, 64, 256), (0.05, 300, 600)),
+                                       "iid", topk=6, seed=31),
+    "many_chunks": synth.small_workload("many_chunks", 1, 4096, 2, 1, (1, 4), "iid", topk=8,
+                                        seed=37),
+    # more than 4096 CSR rows: the budget scan runs over several blocks
+    "scan_blocks": synth.small_workload("scan_blocks", 3, 4096, 4, 2, (2, 6), "iid", topk=5,
+                                        seed=38),
+}
+
+# (name of the budget rule, per-row budgets?, recent window, budget range)
+RULES = {
+    "uniform_recent2": (False, 2, None),
+    "rows_recent0": (True, 0, None),
+    "rows_recent3": (True, 3, None),
+    "rows_clamped_recent1": (True, 1, (-4, 3)),  # out-of-range values, clamped to [1, topk]
+}
+
+_cache = {}
+
+
+class Case:
+    def __init__(self, name):
+        w = CASES[name]
+        say(f"[case] {name}: B={w.batch} L={w.seq_len} Hq={w.num_q_heads} Hkv={w.num_kv_heads}")
+        self.x = x = synth.generate(w)
+        self.w = w
+        self.hq, self.hkv = w.num_q_heads, w.num_kv_heads
+        self.topk = x.topk
+        self.offs = dhsa.ChunkOffsets.from_list(x.offsets, w.seq_len)
+        self.q, self.k, self.v = (dhsa.bf16_from_bits(a) for a in (x.q, x.k, x.v))
+        self.ref = []
+        for b in range(w.batch):
+            q = orc.widen_bf16(x.q[b])
+            k = orc.widen_bf16(x.k[b])
+            qbar, kbar, s64, s32, _rows = orc.build_mask(q, k, x.offsets[b], self.topk)
+            self.ref.append(dict(q=q, k=k, v=orc.widen_bf16(x.v[b]), qbar=qbar, kbar=kbar,
+                                 s64=s64, s32=s32))
+
+    def budgets(self, rule):
+        per_row, recent, rng_range = RULES[rule]
+        if not per_row:
+            return None, None, recent
+        lo, hi = (1, 2 * self.topk - 1) if rng_range is None else \
+            (rng_range[0], rng_range[1] * self.topk)
+        raw = synth.row_budgets(self.offs.num_chunks, self.hq, self.topk, seed=self.w.seed,
+                                lo=lo, hi=hi)
+        return raw, np.clip(raw, 1, self.topk), recent
+
+    def oracle_rows(self, rule, scores_key="s32"):
+        _raw, clamped, recent = self.budgets(rule)
+        rows, pos = [], 0
+        for b, r in enumerate(self.ref):
+            C = r[scores_key].shape[1]
+            if clamped is None:
+                bud = np.full((self.hq, C), self.topk, dtype=np.int64)
+            else:
+                bud = clamped[pos:pos + self.hq * C].reshape(self.hq, C)
+            pos += self.hq * C
+            rows.append(orc.select_topk_ex(r[scores_key], bud, recent))
+        return rows
+
+
+def get_case(name):
+    if name not in _cache:
+        _cache[name] = Case(name)
+    return _cache[name]
+
+
+def _dev_budgets(raw):
+    return None if raw is None else torch.from_numpy(raw).cuda()
+
+
+@pytest.mark.parametrize("rule", list(RULES))
+@pytest.mark.parametrize("name", list(CASES))
+def test_topk_ex_bit_exact_on_oracle_scores(name, rule):
+    c = get_case(name)
+    raw, _clamped, recent = c.budgets(rule)
+    flat = np.concatenate([r["s32"].reshape(-1) for r in c.ref]).astype(np.float32)
+    flat = np.nan_to_num(flat, nan=0.0)
+    say(f"  topk_csr_ex {rule}")
+    csr = dhsa.topk_csr(torch.from_numpy(flat).cuda(), c.offs, c.hq, c.topk,
+                        row_budgets=_dev_budgets(raw), recent=recent)
+    torch.cuda.synchronize()
+    rp_ref, ci_ref = orc.rows_to_csr(c.oracle_rows(rule))
+    rp = csr.row_ptr.cpu().numpy()
+    np.testing.assert_array_equal(rp, rp_ref)
+    np.testing.assert_array_equal(csr.col_idx.cpu().numpy()[:rp[-1]], ci_ref)
+    assert rp[-1] <= csr.nnz  # the capacity bound holds
+
+
+@pytest.mark.parametrize("rule", ["uniform_recent2", "rows_recent3"])
+@pytest.mark.parametrize("name", ["mid_ragged", "scan_blocks"])
+def test_build_mask_ex_matches_stages_and_oracle(name, rule):
+    c = get_case(name)
+    raw, _clamped, recent = c.budgets(rule)
+    bud = _dev_budgets(raw)
+    csr, flat = dhsa.build_mask(c.q, c.k, c.offs, c.topk, return_scores=True,
+                                row_budgets=bud, recent=recent)
+    csr2 = dhsa.topk_csr(flat, c.offs, c.hq, c.topk, row_budgets=bud, recent=recent)
+    torch.cuda.synchronize()
+    rp = csr.row_ptr.cpu().numpy()
+    ci = csr.col_idx.cpu().numpy()[:rp[-1]]
+    # the whole path and the stage call agree bit for bit
+    assert torch.equal(csr.row_ptr, csr2.row_ptr)
+    np.testing.assert_array_equal(ci, csr2.col_idx.cpu().numpy()[:rp[-1]])
+    # against the oracle's float64 selection: equal up to near-ties
+    rows = orc.csr_to_rows(rp, ci, c.offs.num_chunks, c.hq)
+    ref_rows = c.oracle_rows(rule, "s64")
+    G = c.hq // c.hkv
+    near = total = 0
+    for b, r in enumerate(c.ref):
+        qn = np.linalg.norm(r["qbar"], axis=2)
+        kn = np.linalg.norm(r["kbar"], axis=2)
+        for h in range(c.hq):
+            for i, (got, want) in enumerate(zip(rows[b][h], ref_rows[b][h])):
+                total += 1
+                assert len(got) == len(want)
+                if got == want:
+                    continue
+                tol = 2e-5 * qn[h, i] * kn[h // G].max()
+                lo = min(r["s64"][h, i, j] for j in set(want) - set(got))
+                assert all(r["s64"][h, i, j] >= lo - tol for j in set(got) - set(want))
+                near += 1
+    say(f"  near-tie rows: {near} of {total}")
+    assert near <= max(1, total // 1000)
+
+
+@pytest.mark.parametrize("rule", ["uniform_recent2", "rows_recent3"])
+def test_attention_on_ex_mask(rule):
+    c = get_case("mid_ragged")
+    rows = c.oracle_rows(rule, "s64")
+    rp, ci = orc.rows_to_csr(rows)
+    out, lse = dhsa.sparse_prefill(c.q, c.k, c.v, c.offs, dhsa.csr_from_host(rp, ci),
+                                   return_lse=True)
+    torch.cuda.synchronize()
+    got = orc.widen_bf16(to_np_bf16(out))
+    lg = lse.cpu().numpy().astype(np.float64)
+    for b, r in enumerate(c.ref):
+        O, L = orc.sparse_prefill(r["q"], r["k"], r["v"], c.x.offsets[b], rows[b])
+        err = np.abs(got[b] - O)
+        assert np.all(err <= ATOL + RTOL * np.abs(O)), (b, float(err.max()))
+        assert np.all(np.abs(lg[b] - L) <= 2e-3 * (1 + np.abs(L)))
+
+
+def test_window_covering_everything_is_causal_and_budget_one_is_window():
+    c = get_case("tiny_1k")
+    C = int(c.offs.num_chunks[0])
+    flat = np.nan_to_num(np.concatenate([r["s32"].reshape(-1) for r in c.ref]), nan=0.0)
+    flat_t = torch.from_numpy(flat.astype(np.float32)).cuda()
+    # recent >= C: every row keeps 0..i (dense causal chunk mask)
+    csr = dhsa.topk_csr(flat_t, c.offs, c.hq, 1, recent=C + 5)
+    # budget 1 everywhere: exactly the window i-w..i
+    ones = torch.ones(c.hq * C, dtype=torch.int32, device="cuda")
+    csr1 = dhsa.topk_csr(flat_t, c.offs, c.hq, c.topk, row_budgets=ones, recent=2)
+    torch.cuda.synchronize()
+    rows = orc.csr_to_rows(csr.row_ptr.cpu().numpy(), csr.col_idx.cpu().numpy(),
+                           c.offs.num_chunks, c.hq)
+    rows1 = orc.csr_to_rows(csr1.row_ptr.cpu().numpy(), csr1.col_idx.cpu().numpy(),
+                            c.offs.num_chunks, c.hq)
+    for h in range(c.hq):
+        for i in range(C):
+            assert rows[0][h][i] == list(range(i + 1))
+            assert rows1[0][h][i] == list(range(max(0, i - 2), i + 1))
