@@ -107,6 +107,46 @@ def cpu_baseline(x, rows_gpu_unused, hq, hkv, budget_rows=1500, seed=0):
     }
 
 
+def time_variant(dhsa, synth, torch, x, offs, q, k, v, pf, hq, hkv, recent, steps, dev):
+    """The same layer with the widened selection rule: synthetic per-row
+    budgets (uniform in [1, 2 topk - 1], mean topk) capped at 2 topk - 1,
+    plus a window of `recent` chunks before the diagonal
+    (dhsa_build_mask_ex: device prefix sum for row_ptr)."""
+    cap = 2 * x.topk - 1
+    bud = torch.from_numpy(synth.row_budgets(offs.num_chunks, hq, x.topk, seed=x.workload.seed)
+                           ).to(dev)
+    mb = dhsa.MaskBuilder(offs, hq, hkv, cap, device=dev, recent=recent)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        pf(q, k, v, mb(q, k, row_budgets=bud))
+    torch.cuda.synchronize()
+    csr = mb(q, k, row_budgets=bud)
+    torch.cuda.synchronize()
+    rp = csr.row_ptr.cpu().numpy()
+    ci = csr.col_idx.cpu().numpy()[:int(rp[-1])]
+    flops = kept_tile_flops(x.offsets, rp, ci, hq)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s in range(steps):
+        ev[s][0].record(stream)
+        csr = mb(q, k, row_budgets=bud)
+        ev[s][1].record(stream)
+        pf(q, k, v, csr)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    mask_avg = statistics.mean(a.elapsed_time(b) for a, b, _ in ev)
+    attn_avg = statistics.mean(b.elapsed_time(c) for _, b, c in ev)
+    log(f"[bench] variant budgets+recent{recent}: mask {mask_avg:.3f} ms  attention "
+        f"{attn_avg:.3f} ms")
+    mask_bytes = 2 * x.q.shape[0] * x.q.shape[1] * (hq + hkv) * 128 + 4 * (rp.size + ci.size) \
+        + 4 * int(bud.numel())
+    return {"selection": f"per-row budgets in [1, {cap}] (mean {x.topk}), recent {recent}",
+            "steps": steps, "nnz": int(ci.size), "mask_ms": mask_avg, "attention_ms": attn_avg,
+            "kept_tile_TFLOP": flops / 1e12,
+            "TFLOP_per_s": flops / ((mask_avg + attn_avg) * 1e-3) / 1e12,
+            "attention_TFLOP_per_s": flops / (attn_avg * 1e-3) / 1e12,
+            "mask_GBps": mask_bytes / (mask_avg * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +154,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama31_8b_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the per-row-budget + recent-window selection leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -190,6 +232,12 @@ def main():
         except Exception:
             traffic = None
 
+    variants = {}
+    if not args.no_variants:
+        variants["row_budgets_recent2"] = time_variant(
+            dhsa, synth, torch, x, offs, q, k, v, pf, hq, hkv, recent=2,
+            steps=max(2, args.steps // 2), dev=dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
@@ -220,6 +268,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic},
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

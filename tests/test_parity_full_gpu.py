@@ -129,3 +129,72 @@ def test_full_size_layer(name):
             assert np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref)), (name, b, h, i)
         del qf, kf, vf
     say(f"[full] {name}: ok")
+
+
+@pytest.mark.parametrize("name", ["llama31_8b_128k", "ragged_2x64k"])
+def test_full_size_budgets_and_recent(name):
+    """The widened selection rule at full size (per-row budgets with mean
+    topk, capped at 2 topk - 1, and a 2-chunk recent window, as bench.py's
+    variant leg): the GPU selection equals the oracle's on the GPU's own
+    fp32 scores bit for bit, and the oracle's float64 selection up to
+    near-ties; sampled attention rows within the attention bar."""
+    w = synth.WORKLOADS[name]
+    say(f"[full-ex] {name}: generating")
+    x = synth.generate(w)
+    hq, hkv, G = w.num_q_heads, w.num_kv_heads, w.num_q_heads // w.num_kv_heads
+    offs = dhsa.ChunkOffsets.from_list(x.offsets, w.seq_len)
+    q, k, v = (dhsa.bf16_from_bits(a) for a in (x.q, x.k, x.v))
+    cap, recent = 2 * x.topk - 1, 2
+    bud_np = synth.row_budgets(offs.num_chunks, hq, x.topk, seed=w.seed)
+    mb = dhsa.MaskBuilder(offs, hq, hkv, cap, keep_scores=True, recent=recent)
+    pf = dhsa.Prefill(offs, hq, hkv)
+    csr = mb(q, k, row_budgets=torch.from_numpy(bud_np).cuda())
+    out = pf(q, k, v, csr)
+    torch.cuda.synchronize()
+    rp = csr.row_ptr.cpu().numpy()
+    assert rp[-1] <= csr.nnz
+    gpu_rows = orc.csr_to_rows(rp, csr.col_idx.cpu().numpy()[:rp[-1]], offs.num_chunks, hq)
+    scores = mb.scores.cpu().numpy()
+    out_np = to_np_bf16(out)
+    rng = np.random.default_rng(8)
+    spos = bpos = 0
+    for b in range(w.batch):
+        o = x.offsets[b]
+        C = len(o) - 1
+        bud = np.clip(bud_np[bpos:bpos + hq * C].reshape(hq, C), 1, cap)
+        bpos += hq * C
+        gs = scores[spos:spos + hq * C * C].reshape(hq, C, C).astype(np.float64)
+        spos += hq * C * C
+        say(f"[full-ex] {name}: oracle selection on the GPU scores, sequence {b}")
+        assert orc.select_topk_ex(gs, bud, recent) == gpu_rows[b]
+        qf = orc.widen_bf16(x.q[b])
+        kf = orc.widen_bf16(x.k[b])
+        qbar, kbar, s64, _s32, _rows = orc.build_mask(qf, kf, o, x.topk)
+        rows = orc.select_topk_ex(s64, bud, recent)
+        qn = np.linalg.norm(qbar, axis=2)
+        kn = np.linalg.norm(kbar, axis=2)
+        near = 0
+        for h in range(hq):
+            for i in range(C):
+                got, want = gpu_rows[b][h][i], rows[h][i]
+                if got == want:
+                    continue
+                tol = 2e-5 * qn[h, i] * kn[h // G].max()
+                lo = min(s64[h, i, j] for j in set(want) - set(got))
+                assert all(s64[h, i, j] >= lo - tol for j in set(got) - set(want)), (b, h, i)
+                near += 1
+        say(f"[full-ex] {name}: sequence {b}: {near} near-tie rows of {hq * C}")
+        assert near <= max(1, hq * C // 1000)
+        vf = orc.widen_bf16(x.v[b])
+        picks = {(int(rng.integers(0, hq)), int(rng.integers(0, C))) for _ in range(SAMPLES)}
+        picks |= {(0, C - 1), (hq - 1, min(C - 1, recent + 1))}
+        for (h, i) in sorted(picks):
+            if gpu_rows[b][h][i] != rows[h][i]:
+                continue
+            ref, _ = orc.chunk_attention(qf, kf, vf, o, rows[h][i], i, h, h // G,
+                                         1.0 / np.sqrt(128))
+            got = orc.widen_bf16(out_np[b, o[i]:o[i + 1], h])
+            err = np.abs(got - ref)
+            assert np.all(err <= ATOL + RTOL * np.abs(ref)), (name, b, h, i, float(err.max()))
+        del qf, kf, vf
+    say(f"[full-ex] {name}: ok")
