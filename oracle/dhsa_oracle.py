@@ -23,6 +23,11 @@ fusion or reordering beyond what the definition states:
                   Summary, Methodology, Step 2; OpenReview abstract:
                   chunk scores upsampled to token level; DHSA README,
                   "Predictor Checkpoints": a fixed row budget);
+* boundaries   -- greedy non-maximum suppression of per-token boundary
+                  scores into well-separated chunk offsets (Technical
+                  Summary, Methodology, "Dynamic Boundary Detection": the
+                  predictor finalises boundaries with NMS so that they are
+                  well separated and robust to noise);
 * attention    -- dense softmax attention restricted to the token mask
                   (Technical Summary, "Hardware-Agnostic Backends": the SDPA
                   backend is dense masked attention; the tiled backend is its
@@ -331,3 +336,39 @@ def build_mask(q: np.ndarray, k: np.ndarray, offsets: Sequence[int], topk: int):
     s32 = s64.astype(np.float32)
     rows = select_topk(s32, topk)
     return qbar, kbar, s64, s32, rows
+
+
+# --------------------------------------------------------------------------
+# stage 0: boundary finalisation (NMS)
+# --------------------------------------------------------------------------
+
+
+def nms_boundaries(p: np.ndarray, min_gap: int, threshold: float) -> np.ndarray:
+    """Chunk offsets of one sequence from per-token boundary scores.
+
+    p[t] scores "a new chunk starts at token t" (t = 0 .. L-1).  Readings
+    where the pages are silent: the sequence ends 0 and L are boundaries
+    that are always kept; a candidate is a token t with p[t] >= threshold
+    (NaN never is); candidates are visited by score descending, then token
+    ascending, and one is kept when every kept boundary, the two ends
+    included, lies at least min_gap tokens away.  Every chunk then holds at
+    least min_gap tokens.  Returns int64 [0, kept ascending..., L].
+    """
+    p = np.asarray(p, dtype=np.float64)
+    L = p.size
+    if min_gap < 1:
+        raise ValueError("min_gap must be >= 1")
+    if L < 1:
+        raise ValueError("empty sequence")
+    t = np.arange(L)
+    cand = t[(p >= threshold) & (t >= min_gap) & (t <= L - min_gap)]
+    order = cand[np.lexsort((cand, -p[cand]))]
+    kept = [0, L]
+    taken = np.zeros(L + 1, dtype=bool)
+    taken[0] = taken[L] = True
+    for c in order:
+        lo, hi = max(0, c - min_gap + 1), min(L, c + min_gap - 1)
+        if not taken[lo:hi + 1].any():
+            taken[c] = True
+            kept.append(int(c))
+    return np.array(sorted(kept), dtype=np.int64)

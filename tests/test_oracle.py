@@ -394,3 +394,73 @@ def test_budget_recent_vs_brute_force_and_closed_forms():
         k = int(rng.integers(1, 6))
         assert [orc.select_row_ex(S[i], i, k, 0) for i in range(C)] == \
             [_brute_force_row(S[i], i, k) for i in range(C)]
+
+
+# ---------------------------------------------------------------- boundary NMS
+
+
+def test_nms_worked_examples():
+    g = _load("nms_worked_example.json")
+    for case in g["cases"]:
+        got = orc.nms_boundaries(np.array(case["p"]), case["min_gap"], case["threshold"])
+        assert got.tolist() == case["offsets"], (case, got)
+
+
+def _nms_recursive(p, g, tau):
+    # independent formulation: keep the best candidate of the open interval,
+    # cut out everything closer than g to it, recurse on both sides
+    L = len(p)
+
+    def rec(lo, hi):  # candidates in [lo, hi]
+        best = None
+        for t in range(max(lo, g), min(hi, L - g) + 1):
+            if p[t] >= tau and (best is None or p[t] > p[best]):
+                best = t
+        if best is None:
+            return []
+        return rec(lo, best - g) + [best] + rec(best + g, hi)
+
+    return [0] + rec(0, L) + [L]
+
+
+def test_nms_vs_recursive_formulation_and_characterisation():
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        L = int(rng.integers(1, 60))
+        g = int(rng.integers(1, 8))
+        tau = float(rng.choice([0.0, 0.3, 0.5, 0.8]))
+        p = rng.integers(0, 6, size=L) / 5.0   # many exact ties
+        got = orc.nms_boundaries(p, g, tau).tolist()
+        assert got == _nms_recursive(p, g, tau), (p, g, tau)
+        # well separated: every chunk holds >= g tokens (a one-chunk output
+        # of a sequence shorter than g is the exception)
+        assert got[0] == 0 and got[-1] == L
+        if len(got) > 2:
+            assert min(np.diff(got)) >= g
+        # maximal: every candidate left out has a kept boundary closer than
+        # g that ranks above it (or is an end of the sequence)
+        kept = set(got)
+        for t in range(L):
+            if p[t] < tau or t in kept:
+                continue
+            blockers = [s for s in kept if abs(s - t) < g]
+            assert any(s in (0, L) or p[s] > p[t] or (p[s] == p[t] and s < t) for s in blockers)
+
+
+def test_nms_closed_forms():
+    # min_gap 1: every candidate survives
+    p = np.array([0.0, 0.6, 0.7, 0.1, 0.9, 0.5])
+    assert orc.nms_boundaries(p, 1, 0.5).tolist() == [0, 1, 2, 4, 5, 6]
+    # increasing ramp: boundaries every g tokens back from L - g
+    L, g = 100, 7
+    ramp = np.arange(L) / L
+    want = [0] + list(range(L - g, g - 1, -g))[::-1] + [L]
+    assert orc.nms_boundaries(ramp, g, 0.0).tolist() == want
+    # isolated peaks farther apart than g are exactly the boundaries
+    p = np.zeros(200)
+    peaks = [20, 57, 90, 150]
+    p[peaks] = 1.0
+    assert orc.nms_boundaries(p, 16, 0.5).tolist() == [0] + peaks + [200]
+    # NaN never becomes a boundary
+    p[57] = np.nan
+    assert orc.nms_boundaries(p, 16, 0.5).tolist() == [0, 20, 90, 150, 200]
