@@ -15,6 +15,8 @@
  * and three stage calls expose its steps one by one (pool, chunk scores,
  * top-k) for stage-wise checking.  dhsa_build_mask_ex and dhsa_topk_csr_ex
  * widen the selection rule with per-row budgets and a recent-chunk window.
+ * dhsa_nms_boundaries, the step before the path, turns per-token boundary
+ * scores into chunk offsets.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -241,6 +243,44 @@ int dhsa_topk_csr_ex(const float* scores, int32_t batch, int32_t num_q_heads,
                      const int32_t* num_chunks, int32_t topk,
                      const int32_t* row_budgets, int32_t recent, int32_t* row_ptr,
                      int32_t* col_idx, int64_t col_capacity, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Boundary finalisation (the step that produces the chunk offsets)
+ * ---------------------------------------------------------------------- */
+
+/* Entries per sequence that dhsa_nms_boundaries' offsets_out needs:
+ * max(seq_len / min_gap, 1) + 1 (every chunk holds >= min_gap tokens). */
+int dhsa_nms_offsets_stride(int32_t seq_len, int32_t min_gap, int32_t* stride);
+
+/* Bytes of device workspace dhsa_nms_boundaries needs: one state byte per
+ * token (rows 256-byte aligned) and two int32 candidate lists per token. */
+int dhsa_nms_workspace_size(int32_t batch, int32_t seq_len, int32_t min_gap,
+                            size_t* bytes);
+
+/* Non-maximum suppression of per-token boundary scores into chunk offsets
+ * (gist.science Technical Summary, Methodology, "Dynamic Boundary
+ * Detection": the boundary predictor finalises boundaries with NMS so that
+ * they are well separated and robust to noise; the window and threshold
+ * are not given there, so both are arguments).
+ *   scores[b][t] (device fp32 [B][L]) scores "a chunk starts at token t".
+ *   Token t with min_gap <= t <= L - min_gap and scores >= threshold is a
+ *   candidate (NaN never is); candidates are taken by score descending,
+ *   then token ascending, and kept when every kept boundary, the ends 0 and
+ *   L included, is >= min_gap tokens away.
+ * Outputs: offsets_out device int32 [B][offsets_stride]: row b holds
+ *          0, kept tokens ascending, L (C_b + 1 entries; the rest of the
+ *          row is not written); num_chunks_out device int32 [B] = C_b.
+ *          Every chunk holds >= min_gap tokens (or L < 2 min_gap and
+ *          C_b = 1).  The offsets feed dhsa_build_mask after a copy to the
+ *          host (the path sizes its launches from host offsets).
+ * workspace: device, >= dhsa_nms_workspace_size bytes, 256-byte aligned.
+ * Errors: NULL pointers; batch outside [1, DHSA_MAX_BATCH], seq_len < 1,
+ *         min_gap < 1 or a NaN threshold (DHSA_ERR_SHAPE); offsets_stride
+ *         or workspace too small (DHSA_ERR_CAPACITY). */
+int dhsa_nms_boundaries(const float* scores, int32_t batch, int32_t seq_len,
+                        int32_t min_gap, float threshold, int32_t* offsets_out,
+                        int32_t offsets_stride, int32_t* num_chunks_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -156,6 +156,16 @@ int32_t choose_block_m(int32_t batch, const int32_t* num_chunks, const int32_t* 
   return 4 * waves >= 3 * slots ? kBlockMLarge : kBlockMSmall;
 }
 
+int64_t nms_state_stride(int32_t seq_len) { return (int64_t)align_up((size_t)seq_len); }
+
+int check_nms_sizes(int32_t batch, int32_t seq_len, int32_t min_gap) {
+  if (batch < 1 || batch > kMaxBatch)
+    return fail(DHSA_ERR_SHAPE, "batch %d outside [1, %d]", batch, kMaxBatch);
+  if (seq_len < 1) return fail(DHSA_ERR_SHAPE, "seq_len %d < 1", seq_len);
+  if (min_gap < 1) return fail(DHSA_ERR_SHAPE, "min_gap %d < 1", min_gap);
+  return DHSA_OK;
+}
+
 int max_chunks(int32_t batch, const int32_t* num_chunks) {
   int m = 0;
   for (int b = 0; b < batch; ++b) m = num_chunks[b] > m ? num_chunks[b] : m;
@@ -239,6 +249,53 @@ int dhsa_prefill_workspace_size(int32_t batch, int32_t seq_len, const int32_t* n
   // sized for the smaller tile height (the larger needs fewer tiles)
   *bytes = align_up((size_t)query_tiles(batch, num_chunks, chunk_offsets, kBlockMSmall, nullptr) *
                     sizeof(int4));
+  return ok();
+}
+
+int dhsa_nms_offsets_stride(int32_t seq_len, int32_t min_gap, int32_t* stride) {
+  if (stride == nullptr) return fail(DHSA_ERR_NULL_POINTER, "stride is NULL");
+  int s = check_nms_sizes(1, seq_len, min_gap);
+  if (s) return s;
+  const int32_t c = seq_len / min_gap;
+  *stride = (c > 1 ? c : 1) + 1;
+  return ok();
+}
+
+int dhsa_nms_workspace_size(int32_t batch, int32_t seq_len, int32_t min_gap, size_t* bytes) {
+  if (bytes == nullptr) return fail(DHSA_ERR_NULL_POINTER, "bytes is NULL");
+  int s = check_nms_sizes(batch, seq_len, min_gap);
+  if (s) return s;
+  *bytes = align_up((size_t)batch * nms_state_stride(seq_len)) +
+           align_up((size_t)batch * 2 * seq_len * sizeof(int32_t));
+  return ok();
+}
+
+int dhsa_nms_boundaries(const float* scores, int32_t batch, int32_t seq_len, int32_t min_gap,
+                        float threshold, int32_t* offsets_out, int32_t offsets_stride,
+                        int32_t* num_chunks_out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!scores || !offsets_out || !num_chunks_out || !workspace)
+    return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
+  int s = check_nms_sizes(batch, seq_len, min_gap);
+  if (s) return s;
+  if (!(threshold == threshold)) return fail(DHSA_ERR_SHAPE, "threshold is NaN");
+  int32_t need_stride;
+  s = dhsa_nms_offsets_stride(seq_len, min_gap, &need_stride);
+  if (s) return s;
+  if (offsets_stride < need_stride)
+    return fail(DHSA_ERR_CAPACITY, "offsets_stride %d < %d", offsets_stride, need_stride);
+  size_t need;
+  s = dhsa_nms_workspace_size(batch, seq_len, min_gap, &need);
+  if (s) return s;
+  if (workspace_bytes < need)
+    return fail(DHSA_ERR_CAPACITY, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DHSA_ERR_CAPACITY, "workspace not %zu-byte aligned", kAlign);
+  const int64_t sstride = nms_state_stride(seq_len);
+  hipError_t e = launch_nms(scores, batch, seq_len, min_gap, threshold, offsets_out,
+                            offsets_stride, num_chunks_out, workspace, sstride,
+                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "boundary NMS launch");
   return ok();
 }
 

@@ -58,6 +58,13 @@ hipError_t launch_topk(const float* scores, const SeqTable& st, int32_t hq,
                        const int32_t* budgets, int32_t max_chunks, int32_t* row_ptr,
                        int32_t* col_idx, hipStream_t stream);
 
+// workspace: batch * state_stride bytes of per-token state, then
+// batch * 2 * seq_len int32 candidate lists
+hipError_t launch_nms(const float* scores, int32_t batch, int32_t seq_len, int32_t min_gap,
+                      float threshold, int32_t* offsets_out, int32_t stride,
+                      int32_t* num_chunks_out, void* workspace, int64_t state_stride,
+                      hipStream_t stream);
+
 hipError_t launch_plan_tiles(const int32_t* offs_dev, const SeqTable& st,
                              int4* tiles, int32_t block_m, hipStream_t stream);
 

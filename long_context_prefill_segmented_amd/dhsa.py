@@ -61,6 +61,10 @@ _SIGNATURES = {
     "dhsa_topk_csr": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _i64, _vp]),
     "dhsa_topk_csr_ex": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64,
                                         _vp]),
+    "dhsa_nms_offsets_stride": (ctypes.c_int, [_i32, _i32, _pi32]),
+    "dhsa_nms_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _psz]),
+    "dhsa_nms_boundaries": (ctypes.c_int, [_vp, _i32, _i32, _i32, _f32, _vp, _i32, _vp, _vp, _sz,
+                                           _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -327,6 +331,48 @@ def topk_csr(scores, offsets: ChunkOffsets, hq: int, topk: int, stream=None,
                                    _dptr(csr.row_ptr), _dptr(csr.col_idx), csr.col_idx.numel(),
                                    _stream_ptr(stream)))
     return csr
+
+
+class BoundaryNMS:
+    """Preallocated buffers for repeated dhsa_nms_boundaries calls on one
+    shape: per-token boundary scores [B, L] -> chunk offsets."""
+
+    def __init__(self, batch: int, seq_len: int, min_gap: int, threshold: float, device="cuda"):
+        torch = _torch()
+        self.batch, self.seq_len, self.min_gap = batch, seq_len, min_gap
+        self.threshold = float(threshold)
+        st = _i32()
+        check(lib.dhsa_nms_offsets_stride(seq_len, min_gap, ctypes.byref(st)))
+        self.stride = st.value
+        n = _sz()
+        check(lib.dhsa_nms_workspace_size(batch, seq_len, min_gap, ctypes.byref(n)))
+        self.ws = _workspace(n.value, device)
+        self.offsets = torch.empty((batch, self.stride), dtype=torch.int32, device=device)
+        self.num_chunks = torch.empty(batch, dtype=torch.int32, device=device)
+
+    def __call__(self, scores, stream=None):
+        torch = _torch()
+        if (scores.dtype != torch.float32 or not scores.is_contiguous() or not scores.is_cuda
+                or tuple(scores.shape) != (self.batch, self.seq_len)):
+            raise ValueError(f"scores must be contiguous CUDA float32 [{self.batch}, {self.seq_len}]")
+        check(lib.dhsa_nms_boundaries(_dptr(scores), self.batch, self.seq_len, self.min_gap,
+                                      self.threshold, _dptr(self.offsets), self.stride,
+                                      _dptr(self.num_chunks), _dptr(self.ws), self.ws.numel(),
+                                      _stream_ptr(stream)))
+        return self.offsets, self.num_chunks
+
+    def to_chunk_offsets(self, device="cuda") -> "ChunkOffsets":
+        """Copies the last result to the host (synchronising) as ChunkOffsets."""
+        nc = self.num_chunks.cpu().numpy()
+        offs = self.offsets.cpu().numpy()
+        return ChunkOffsets.from_list([offs[b, :int(nc[b]) + 1] for b in range(self.batch)],
+                                      self.seq_len, device=device)
+
+
+def nms_boundaries(scores, min_gap: int, threshold: float, stream=None):
+    """dhsa_nms_boundaries: returns (offsets [B, stride], num_chunks [B]) on the device."""
+    B, L = scores.shape
+    return BoundaryNMS(B, L, min_gap, threshold, device=scores.device)(scores, stream)
 
 
 def csr_from_host(row_ptr: np.ndarray, col_idx: np.ndarray, device="cuda") -> CSR:

@@ -284,3 +284,28 @@ def row_budgets(num_chunks: Sequence[int], hq: int, topk: int, seed: int,
     rng = np.random.Generator(np.random.PCG64([seed, 0xB0D6]))
     total = int(hq * sum(int(c) for c in num_chunks))
     return rng.integers(lo, hi + 1, size=total, dtype=np.int64).astype(np.int32)
+
+
+def boundary_scores(offsets: Sequence[np.ndarray], seq_len: int, seed: int,
+                    spurious_per_token: float = 1.0 / 4000) -> np.ndarray:
+    """Synthetic per-token boundary scores [B, L] float32 in [0, 1), standing in
+    for a trained boundary predictor's output (no weights are available).
+
+    Background tokens draw U(0, 0.45).  At every chunk start s of `offsets`
+    (s > 0) the score peaks at U(0.85, 1.0), and its two neighbours s - 1 and
+    s + 1 form shoulders U(0.5, 0.8): above a 0.5 threshold, below the peak.
+    Isolated spurious spikes U(0.5, 1.0) appear at `spurious_per_token`."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0xB0B]))
+    B = len(offsets)
+    p = rng.uniform(0.0, 0.45, size=(B, seq_len)).astype(np.float32)
+    for b, o in enumerate(offsets):
+        starts = np.asarray(o[1:-1], dtype=np.int64)
+        for d in (-1, 1):
+            nb = starts + d
+            nb = nb[(nb > 0) & (nb < seq_len)]
+            p[b, nb] = rng.uniform(0.5, 0.8, size=nb.size)
+        p[b, starts] = rng.uniform(0.85, 1.0, size=starts.size)
+        n_sp = rng.binomial(seq_len, spurious_per_token)
+        sp = rng.integers(1, seq_len, size=n_sp)
+        p[b, sp] = rng.uniform(0.5, 1.0, size=n_sp)
+    return p

@@ -211,3 +211,35 @@ def test_ex_calls_reject_bad_arguments():
     assert bm(recent=-2) == ETOPK
     assert bm(topk=0, budgets=FAKE) == ETOPK
     assert bm(topk=2, recent=1, cap=23) == ECAP             # nnz bound = 4 * (1 + 2 + 3) = 24
+
+
+def test_nms_sizes():
+    st = ctypes.c_int32()
+    for L, g, want in ((131072, 32, 4097), (100, 7, 15), (5, 8, 2), (16, 8, 3)):
+        assert lib.dhsa_nms_offsets_stride(L, g, ctypes.byref(st)) == OK
+        assert st.value == want
+    assert lib.dhsa_nms_offsets_stride(100, 0, ctypes.byref(st)) == ESHAPE
+    n = ctypes.c_size_t()
+    assert lib.dhsa_nms_workspace_size(2, 1000, 8, ctypes.byref(n)) == OK
+    assert n.value == 2 * 1024 + (2 * 2 * 1000 * 4 + 255) // 256 * 256
+    assert lib.dhsa_nms_workspace_size(0, 1000, 8, ctypes.byref(n)) == ESHAPE
+
+
+@cpu_only
+def test_nms_rejects_bad_arguments():
+    def call(**kw):
+        a = dict(scores=FAKE, batch=1, L=1000, g=8, tau=0.5, out=FAKE, stride=126, nc=FAKE,
+                 ws=FAKE, ws_bytes=1 << 20)
+        a.update(kw)
+        return lib.dhsa_nms_boundaries(a["scores"], a["batch"], a["L"], a["g"], a["tau"],
+                                       a["out"], a["stride"], a["nc"], a["ws"], a["ws_bytes"],
+                                       None)
+    assert call(scores=None) == ENULL
+    assert call(nc=None) == ENULL
+    assert call(g=0) == ESHAPE
+    assert call(L=0) == ESHAPE
+    assert call(batch=65) == ESHAPE
+    assert call(tau=float("nan")) == ESHAPE
+    assert call(stride=125) == ECAP          # 1000 // 8 + 1 = 126
+    assert call(ws_bytes=100) == ECAP
+    assert call(ws=FAKE + 4) == ECAP
