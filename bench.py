@@ -147,6 +147,66 @@ def time_variant(dhsa, synth, torch, x, offs, q, k, v, pf, hq, hkv, recent, step
             "mask_GBps": mask_bytes / (mask_avg * 1e-3) / 1e9}
 
 
+def time_nms(dhsa, synth, torch, x, dev, min_gap=32, threshold=0.5, steps=20):
+    """Boundary finalisation on synthetic predictor scores for the same
+    sequences (peaks at the layer's chunk starts, shoulders, spurious
+    spikes): dhsa_nms_boundaries, one workgroup per sequence."""
+    w = x.workload
+    p = torch.from_numpy(synth.boundary_scores(x.offsets, w.seq_len, seed=w.seed)).to(dev)
+    nms = dhsa.BoundaryNMS(w.batch, w.seq_len, min_gap, threshold, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        nms(p)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for s in range(steps):
+        ev[s][0].record(stream)
+        nms(p)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = statistics.mean(a.elapsed_time(b) for a, b in ev)
+    nc = [int(c) for c in nms.num_chunks.cpu().numpy()]
+    log(f"[bench] boundary NMS: {ms * 1e3:.1f} us  chunks {nc}")
+    nbytes = 4 * w.batch * w.seq_len + 4 * sum(c + 1 for c in nc)
+    return {"min_gap": min_gap, "threshold": threshold, "steps": steps, "ms": ms,
+            "num_chunks": nc, "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+
+def time_batched_loop(dhsa, synth, torch, dev, name="ragged_2x64k", steps=5):
+    """The batched workload through dhsa_layer_forward twice: as the
+    sequential per-sequence loop (workspace for one sequence) and as one pass
+    over the batch; per-step time and the peak device memory above the
+    resident inputs (torch's allocator holds every device buffer)."""
+    w = synth.WORKLOADS[name]
+    x = synth.generate(w)
+    offs = dhsa.ChunkOffsets.from_list(x.offsets, w.seq_len, device=dev)
+    q, k, v = (dhsa.bf16_from_bits(a, dev) for a in (x.q, x.k, x.v))
+    stream = torch.cuda.current_stream()
+    res = {"workload": name, "batch": w.batch, "seq_len": w.seq_len, "topk": x.topk}
+    for label, g in (("sequential", 1), ("one_pass", w.batch)):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        layer = dhsa.Layer(offs, w.num_q_heads, w.num_kv_heads, x.topk, max_group=g, device=dev)
+        layer(q, k, v)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for s in range(steps):
+            ev[s][0].record(stream)
+            layer(q, k, v)
+            ev[s][1].record(stream)
+        torch.cuda.synchronize()
+        ms = statistics.mean(a.elapsed_time(b) for a, b in ev)
+        peak = torch.cuda.max_memory_allocated() - base
+        log(f"[bench] batched {label}: {ms:.3f} ms/layer, {layer.num_groups} groups, "
+            f"peak {peak / 2**20:.1f} MiB above inputs")
+        res[label] = {"ms": ms, "groups": layer.num_groups,
+                      "workspace_MiB": layer.ws.numel() / 2**20, "peak_MiB": peak / 2**20}
+        del layer
+    res["inputs_MiB"] = (q.numel() + k.numel() + v.numel()) * 2 / 2**20
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +297,8 @@ def main():
         variants["row_budgets_recent2"] = time_variant(
             dhsa, synth, torch, x, offs, q, k, v, pf, hq, hkv, recent=2,
             steps=max(2, args.steps // 2), dev=dev)
+        variants["boundary_nms"] = time_nms(dhsa, synth, torch, x, dev)
+        variants["batched_loop"] = time_batched_loop(dhsa, synth, torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -245,6 +245,46 @@ int dhsa_topk_csr_ex(const float* scores, int32_t batch, int32_t num_q_heads,
                      int32_t* col_idx, int64_t col_capacity, void* stream);
 
 /* ------------------------------------------------------------------------
+ * A whole layer over a batch, within a workspace budget
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace dhsa_layer_forward needs to process any
+ * max_group consecutive sequences in one pass (mask workspace, CSR buffers
+ * and attention workspace of the largest such group, 256-byte aligned
+ * parts).  max_group = 1 sizes the sequential per-sequence loop;
+ * max_group >= batch sizes one pass over the whole batch.  recent as in
+ * dhsa_build_mask_ex. */
+int dhsa_layer_workspace_size(int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              const int32_t* num_chunks, const int32_t* chunk_offsets,
+                              int32_t topk, int32_t recent, int32_t max_group,
+                              size_t* bytes);
+
+/* One attention layer: dhsa_build_mask_ex then dhsa_sparse_prefill, run over
+ * groups of consecutive sequences, each group as large as the workspace
+ * allows (DHSA paper summary, Efficiency, "Batching": under a memory limit
+ * the batch is processed sequence by sequence in a plain loop rather than
+ * in one batched call).  Groups run in order on `stream` and reuse the one
+ * workspace; results equal those of one pass over the whole batch.
+ * Inputs, outputs and selection arguments as dhsa_build_mask_ex and
+ * dhsa_sparse_prefill (row_budgets nullable, in CSR row order of the whole
+ * batch).  num_groups (host, nullable) receives the number of groups.
+ * workspace: device, 256-byte aligned; workspace_bytes must hold at least
+ * the largest single sequence (dhsa_layer_workspace_size with max_group 1).
+ * Errors: as the two calls, checked for the whole batch before anything is
+ * enqueued; DHSA_ERR_CAPACITY when one sequence alone does not fit.  A
+ * DHSA_ERR_HIP from a later group leaves the earlier groups enqueued. */
+int dhsa_layer_forward(const void* q, const void* k, const void* v,
+                       int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim,
+                       const int32_t* num_chunks, const int32_t* chunk_offsets,
+                       const int32_t* chunk_offsets_dev, int32_t topk,
+                       const int32_t* row_budgets, int32_t recent,
+                       float softmax_scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes,
+                       int32_t* num_groups, void* stream);
+
+/* ------------------------------------------------------------------------
  * Boundary finalisation (the step that produces the chunk offsets)
  * ---------------------------------------------------------------------- */
 

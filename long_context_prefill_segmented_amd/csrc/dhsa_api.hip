@@ -10,7 +10,6 @@
 #include "dhsa_internal.h"
 
 namespace dhsa {
-namespace {
 
 thread_local char g_err[512] = "";
 
@@ -26,6 +25,8 @@ int ok() {
   g_err[0] = '\0';
   return DHSA_OK;
 }
+
+namespace {
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(DHSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -194,7 +195,7 @@ const char* dhsa_status_string(int status) {
   }
 }
 
-const char* dhsa_last_error(void) { return g_err; }
+const char* dhsa_last_error(void) { return dhsa::g_err; }
 
 int dhsa_version(void) { return 101; }
 

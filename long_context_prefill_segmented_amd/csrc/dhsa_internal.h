@@ -65,6 +65,10 @@ hipError_t launch_nms(const float* scores, int32_t batch, int32_t seq_len, int32
                       int32_t* num_chunks_out, void* workspace, int64_t state_stride,
                       hipStream_t stream);
 
+// host side: set the calling thread's error message and return status
+int fail(int status, const char* fmt, ...);
+int ok();
+
 hipError_t launch_plan_tiles(const int32_t* offs_dev, const SeqTable& st,
                              int4* tiles, int32_t block_m, hipStream_t stream);
 

@@ -61,6 +61,11 @@ _SIGNATURES = {
     "dhsa_topk_csr": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _i64, _vp]),
     "dhsa_topk_csr_ex": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64,
                                         _vp]),
+    "dhsa_layer_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32,
+                                                 _i32, _i32, _psz]),
+    "dhsa_layer_forward": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                          _vp, _i32, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _pi32,
+                                          _vp]),
     "dhsa_nms_offsets_stride": (ctypes.c_int, [_i32, _i32, _pi32]),
     "dhsa_nms_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _psz]),
     "dhsa_nms_boundaries": (ctypes.c_int, [_vp, _i32, _i32, _i32, _f32, _vp, _i32, _vp, _vp, _sz,
@@ -331,6 +336,50 @@ def topk_csr(scores, offsets: ChunkOffsets, hq: int, topk: int, stream=None,
                                    _dptr(csr.row_ptr), _dptr(csr.col_idx), csr.col_idx.numel(),
                                    _stream_ptr(stream)))
     return csr
+
+
+def layer_workspace_size(offsets: ChunkOffsets, hq: int, hkv: int, topk: int, recent: int = 0,
+                         max_group: int = 1) -> int:
+    n = _sz()
+    check(lib.dhsa_layer_workspace_size(offsets.batch, offsets.seq_len, hq, hkv, HEAD_DIM,
+                                        _np_ptr(offsets.num_chunks), _np_ptr(offsets.host), topk,
+                                        recent, max_group, ctypes.byref(n)))
+    return n.value
+
+
+class Layer:
+    """dhsa_layer_forward with a fixed workspace: the whole layer (mask and
+    attention) over the batch, in groups of consecutive sequences that fit
+    the workspace.  max_group = 1 sizes it for the sequential per-sequence
+    loop, max_group = batch for one pass; workspace_bytes overrides both."""
+
+    def __init__(self, offsets: ChunkOffsets, hq: int, hkv: int, topk: int, recent: int = 0,
+                 max_group: int = 1, workspace_bytes: Optional[int] = None, device="cuda",
+                 with_lse: bool = False, softmax_scale: float = 0.0):
+        torch = _torch()
+        self.offsets, self.hq, self.hkv, self.topk, self.recent = offsets, hq, hkv, topk, recent
+        self.scale = float(softmax_scale)
+        if workspace_bytes is None:
+            workspace_bytes = layer_workspace_size(offsets, hq, hkv, topk, recent, max_group)
+        self.ws = _workspace(workspace_bytes, device)
+        B, L = offsets.batch, offsets.seq_len
+        self.out = torch.empty((B, L, hq, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((B, hq, L), dtype=torch.float32, device=device) if with_lse else None
+        self.num_groups = 0
+
+    def __call__(self, q, k, v, row_budgets=None, stream=None):
+        _check_qkv(q, k, v)
+        o = self.offsets
+        R = self.hq * int(o.num_chunks.sum())
+        ng = _i32()
+        check(lib.dhsa_layer_forward(
+            _dptr(q), _dptr(k), _dptr(v), o.batch, o.seq_len, self.hq, self.hkv, HEAD_DIM,
+            _np_ptr(o.num_chunks), _np_ptr(o.host), _dptr(o.device), self.topk,
+            _budgets_ptr(row_budgets, R), self.recent, self.scale, _dptr(self.out),
+            _dptr(self.lse) if self.lse is not None else None, _dptr(self.ws), self.ws.numel(),
+            ctypes.byref(ng), _stream_ptr(stream)))
+        self.num_groups = ng.value
+        return (self.out, self.lse) if self.lse is not None else self.out
 
 
 class BoundaryNMS:

@@ -243,3 +243,58 @@ def test_nms_rejects_bad_arguments():
     assert call(stride=125) == ECAP          # 1000 // 8 + 1 = 126
     assert call(ws_bytes=100) == ECAP
     assert call(ws=FAKE + 4) == ECAP
+
+
+def _layer_ws(nc, offs, hq=4, hkv=2, k=2, recent=0, group=1, L=100):
+    n = ctypes.c_size_t()
+    nc = _arr(nc)
+    offs = _arr(offs)
+    s = lib.dhsa_layer_workspace_size(nc.size, L, hq, hkv, 128, nc.ctypes.data, offs.ctypes.data,
+                                      k, recent, group, ctypes.byref(n))
+    return s, n.value
+
+
+def test_layer_workspace_size_parts():
+    def al(x):
+        return (x + 255) // 256 * 256
+    nc = [3, 2]
+    offs = [0, 10, 50, 100, 0, 60, 100]
+
+    def single(c, offsets):
+        # mask (pooled Q, K, scores) + row_ptr + col_idx + query tiles
+        mask = al(4 * c * 128 * 4) + al(2 * c * 128 * 4) + al(4 * c * c * 4)
+        nnz = 4 * sum(min(2, i + 1) for i in range(c))
+        tiles = sum((offsets[i + 1] - offsets[i] + 127) // 128 for i in range(c))
+        return al(mask) + al(4 * (4 * c + 1)) + al(4 * nnz) + al(16 * tiles)
+    s, n1 = _layer_ws(nc, offs, group=1)
+    assert s == OK and n1 == max(single(3, offs[:4]), single(2, offs[4:]))
+    s, n2 = _layer_ws(nc, offs, group=2)
+    mask = al(4 * 5 * 128 * 4) + al(2 * 5 * 128 * 4) + al(4 * (9 + 4) * 4)
+    nnz = 4 * (5 + 3)
+    assert s == OK and n2 == al(mask) + al(4 * 21) + al(4 * nnz) + al(16 * 5)
+    assert _layer_ws(nc, offs, group=0)[0] == ESHAPE
+    assert _layer_ws(nc, offs, k=0)[0] == ETOPK
+    assert _layer_ws(nc, [0, 10, 50, 99, 0, 60, 100])[0] == EOFF
+
+
+@cpu_only
+def test_layer_forward_rejects_bad_arguments():
+    nc = _arr([3, 2])
+    offs = _arr([0, 10, 50, 100, 0, 60, 100])
+    s, need1 = _layer_ws([3, 2], list(offs), group=1)
+
+    def call(**kw):
+        a = dict(q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, scale=0.0, topk=2, recent=0)
+        a.update(kw)
+        return lib.dhsa_layer_forward(a["q"], FAKE, FAKE, 2, 100, 4, 2, 128, nc.ctypes.data,
+                                      offs.ctypes.data, FAKE, a["topk"], None, a["recent"],
+                                      a["scale"], a["out"], None, a["ws"], a["ws_bytes"], None,
+                                      None)
+    assert call(q=None) == ENULL
+    assert call(out=None) == ENULL
+    assert call(scale=float("nan")) == ESHAPE
+    assert call(topk=0) == ETOPK
+    assert call(recent=-1) == ETOPK
+    assert call(ws=FAKE + 16) == ECAP
+    assert call(ws_bytes=need1 - 1) == ECAP
+    assert b"alone" in lib.dhsa_last_error()
