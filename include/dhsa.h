@@ -69,6 +69,7 @@ extern "C" {
 #define DHSA_HEAD_DIM 128
 #define DHSA_MAX_BATCH 64
 #define DHSA_MAX_CHUNKS 2048
+#define DHSA_NMS_MAX_LEN 524288
 
 typedef enum dhsa_status {
   DHSA_OK = 0,
@@ -292,8 +293,8 @@ int dhsa_layer_forward(const void* q, const void* k, const void* v,
  * max(seq_len / min_gap, 1) + 1 (every chunk holds >= min_gap tokens). */
 int dhsa_nms_offsets_stride(int32_t seq_len, int32_t min_gap, int32_t* stride);
 
-/* Bytes of device workspace dhsa_nms_boundaries needs: one state byte per
- * token (rows 256-byte aligned) and two int32 candidate lists per token. */
+/* Bytes of device workspace dhsa_nms_boundaries needs: two int32 candidate
+ * lists per sequence, seq_len entries each. */
 int dhsa_nms_workspace_size(int32_t batch, int32_t seq_len, int32_t min_gap,
                             size_t* bytes);
 
@@ -315,8 +316,10 @@ int dhsa_nms_workspace_size(int32_t batch, int32_t seq_len, int32_t min_gap,
  *          host (the path sizes its launches from host offsets).
  * workspace: device, >= dhsa_nms_workspace_size bytes, 256-byte aligned.
  * Errors: NULL pointers; batch outside [1, DHSA_MAX_BATCH], seq_len < 1,
- *         min_gap < 1 or a NaN threshold (DHSA_ERR_SHAPE); offsets_stride
- *         or workspace too small (DHSA_ERR_CAPACITY). */
+ *         min_gap < 1 or a NaN threshold (DHSA_ERR_SHAPE); seq_len >
+ *         DHSA_NMS_MAX_LEN (DHSA_ERR_UNSUPPORTED: the per-token state of a
+ *         sequence lives in one workgroup's LDS, 2 bits per token);
+ *         offsets_stride or workspace too small (DHSA_ERR_CAPACITY). */
 int dhsa_nms_boundaries(const float* scores, int32_t batch, int32_t seq_len,
                         int32_t min_gap, float threshold, int32_t* offsets_out,
                         int32_t offsets_stride, int32_t* num_chunks_out,

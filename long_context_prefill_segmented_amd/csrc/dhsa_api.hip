@@ -157,12 +157,12 @@ int32_t choose_block_m(int32_t batch, const int32_t* num_chunks, const int32_t* 
   return 4 * waves >= 3 * slots ? kBlockMLarge : kBlockMSmall;
 }
 
-int64_t nms_state_stride(int32_t seq_len) { return (int64_t)align_up((size_t)seq_len); }
-
 int check_nms_sizes(int32_t batch, int32_t seq_len, int32_t min_gap) {
   if (batch < 1 || batch > kMaxBatch)
     return fail(DHSA_ERR_SHAPE, "batch %d outside [1, %d]", batch, kMaxBatch);
   if (seq_len < 1) return fail(DHSA_ERR_SHAPE, "seq_len %d < 1", seq_len);
+  if (seq_len > kNmsMaxLen)
+    return fail(DHSA_ERR_UNSUPPORTED, "seq_len %d > %d for boundary NMS", seq_len, kNmsMaxLen);
   if (min_gap < 1) return fail(DHSA_ERR_SHAPE, "min_gap %d < 1", min_gap);
   return DHSA_OK;
 }
@@ -266,8 +266,7 @@ int dhsa_nms_workspace_size(int32_t batch, int32_t seq_len, int32_t min_gap, siz
   if (bytes == nullptr) return fail(DHSA_ERR_NULL_POINTER, "bytes is NULL");
   int s = check_nms_sizes(batch, seq_len, min_gap);
   if (s) return s;
-  *bytes = align_up((size_t)batch * nms_state_stride(seq_len)) +
-           align_up((size_t)batch * 2 * seq_len * sizeof(int32_t));
+  *bytes = align_up((size_t)batch * 2 * seq_len * sizeof(int32_t));
   return ok();
 }
 
@@ -292,9 +291,8 @@ int dhsa_nms_boundaries(const float* scores, int32_t batch, int32_t seq_len, int
     return fail(DHSA_ERR_CAPACITY, "workspace %zu < %zu bytes", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return fail(DHSA_ERR_CAPACITY, "workspace not %zu-byte aligned", kAlign);
-  const int64_t sstride = nms_state_stride(seq_len);
   hipError_t e = launch_nms(scores, batch, seq_len, min_gap, threshold, offsets_out,
-                            offsets_stride, num_chunks_out, workspace, sstride,
+                            offsets_stride, num_chunks_out, workspace,
                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "boundary NMS launch");
   return ok();

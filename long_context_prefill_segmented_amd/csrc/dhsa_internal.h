@@ -58,12 +58,12 @@ hipError_t launch_topk(const float* scores, const SeqTable& st, int32_t hq,
                        const int32_t* budgets, int32_t max_chunks, int32_t* row_ptr,
                        int32_t* col_idx, hipStream_t stream);
 
-// workspace: batch * state_stride bytes of per-token state, then
-// batch * 2 * seq_len int32 candidate lists
+// Longest sequence the boundary NMS takes: its per-token 2-bit states fill
+// 128 KB of LDS.  workspace: batch * 2 * seq_len int32 candidate lists.
+constexpr int kNmsMaxLen = DHSA_NMS_MAX_LEN;
 hipError_t launch_nms(const float* scores, int32_t batch, int32_t seq_len, int32_t min_gap,
                       float threshold, int32_t* offsets_out, int32_t stride,
-                      int32_t* num_chunks_out, void* workspace, int64_t state_stride,
-                      hipStream_t stream);
+                      int32_t* num_chunks_out, void* workspace, hipStream_t stream);
 
 // host side: set the calling thread's error message and return status
 int fail(int status, const char* fmt, ...);

@@ -16,14 +16,17 @@
 // exactly when every higher-ranked candidate near it is decided, and then as
 // the greedy pass decides it, so the rounds end with the greedy set; each
 // round keeps at least the highest-ranked live candidate, so they end.
-// A round costs O(live candidates + kept * min_gap); the number of rounds is
+// A round costs O(live candidates * min_gap / 16); the number of rounds is
 // the longest chain of ever-higher candidates spaced under min_gap apart
 // (a few for noisy peaks, up to L / min_gap for a monotone ramp).
 //
-// One workgroup per sequence.  The per-token state (0 none or dead, 1 live,
-// 2 kept) and two live-candidate lists sit in the workspace; lists are
-// compacted per wave with a ballot and one LDS atomic, since their order does
-// not matter; the final pass compacts kept tokens in token order.
+// One workgroup per sequence.  Every token's state (0 none or dead, 1 live,
+// 2 kept) is a 2-bit field in LDS, 16 tokens to a 32-bit word, so a
+// neighbourhood of 2 min_gap - 1 tokens is a handful of word reads and the
+// live candidates near a token are found with bit operations; a transition
+// is one LDS atomic on its word.  The live-candidate lists sit in the
+// workspace (their order does not matter: waves append with one LDS atomic);
+// the final pass emits kept tokens in token order with a block-wide scan.
 #include "dhsa_internal.h"
 
 namespace dhsa {
@@ -31,6 +34,7 @@ namespace {
 
 constexpr int kNmsThreads = 1024;
 constexpr int kNmsWaves = kNmsThreads / 64;
+constexpr int kNmsWords = kNmsMaxLen / 16;  // 2 bits per token
 
 __device__ __forceinline__ bool ranks_above(float pa, int a, float pb, int b) {
   return pa > pb || (pa == pb && a < b);
@@ -40,35 +44,96 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return lane ? ((~0ull) >> (64 - lane)) : 0ull;
 }
 
+// exclusive prefix sum across the wave, and the wave's total
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  *total = __shfl(incl, 63, 64);
+  return incl - v;
+}
+
+// both bits of the 2-bit fields of word wd whose tokens lie in [lo, hi]
+__device__ __forceinline__ uint32_t range_fields(int wd, int lo, int hi) {
+  const int f0 = lo > 16 * wd ? lo - 16 * wd : 0;
+  const int f1 = hi < 16 * wd + 15 ? hi - 16 * wd : 15;
+  const uint32_t upto = f1 == 15 ? 0xffffffffu : ((1u << (2 * f1 + 2)) - 1u);
+  const uint32_t below = (1u << (2 * f0)) - 1u;
+  return upto & ~below;
+}
+
+__device__ __forceinline__ uint32_t field_of(const uint32_t* sw, int t) {
+  return (sw[t >> 4] >> (2 * (t & 15))) & 3u;
+}
+
 __global__ __launch_bounds__(kNmsThreads) void nms_kernel(
     const float* __restrict__ scores, int32_t seq_len, int32_t min_gap, float threshold,
     int32_t* __restrict__ offsets_out, int32_t stride, int32_t* __restrict__ num_chunks_out,
-    uint8_t* state_ws, int32_t* list_ws, int64_t state_stride) {
+    int32_t* list_ws) {
+  __shared__ uint32_t sw[kNmsWords];
   __shared__ int s_count;
   __shared__ int s_wsum[kNmsWaves];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int L = seq_len, g = min_gap;
+  const int nw = (L + 15) / 16;
   const float* p = scores + (size_t)b * L;
-  uint8_t* st = state_ws + (size_t)b * state_stride;
   int32_t* la = list_ws + (size_t)b * 2 * L;
   int32_t* lb = la + L;
 
-  // ---- candidates
+  // ---- candidates: kWordsPerStep state words (16 tokens each) per thread
+  // and step, their score loads all issued before any is used
   if (tid == 0) s_count = 0;
   __syncthreads();
-  for (int t0 = 0; t0 < L; t0 += kNmsThreads) {
-    const int t = t0 + tid;
-    bool cand = false;
-    if (t < L) {
-      cand = t >= g && t <= L - g && p[t] >= threshold;
-      st[t] = cand ? 1 : 0;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+  constexpr int kWordsPerStep = 4;
+  for (int w0 = 0; w0 < nw; w0 += kWordsPerStep * kNmsThreads) {
+    float x[kWordsPerStep][16];
+#pragma unroll
+    for (int j = 0; j < kWordsPerStep; ++j) {
+      const int w = w0 + j * kNmsThreads + tid;
+      const int t0 = 16 * w;
+      if (w < nw && vec_ok && t0 + 16 <= L) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 f = *reinterpret_cast<const float4*>(p + t0 + 4 * e);
+          x[j][4 * e] = f.x;
+          x[j][4 * e + 1] = f.y;
+          x[j][4 * e + 2] = f.z;
+          x[j][4 * e + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[j][e] = (w < nw && t0 + e < L) ? p[t0 + e] : 0.f;
+      }
     }
-    const uint64_t m = __ballot(cand);
-    int base = 0;
-    if (lane == 0 && m) base = atomicAdd(&s_count, __popcll(m));
-    base = __shfl(base, 0);
-    if (cand) la[base + __popcll(m & lanes_below(lane))] = t;
+#pragma unroll
+    for (int j = 0; j < kWordsPerStep; ++j) {
+      const int w = w0 + j * kNmsThreads + tid;
+      const int t0 = 16 * w;
+      uint32_t word = 0;
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = t0 + e;
+        const bool cand = w < nw && t >= g && t <= L - g && x[j][e] >= threshold;
+        word |= cand ? (1u << (2 * e)) : 0u;
+        cnt += cand ? 1 : 0;
+      }
+      if (w < nw) sw[w] = word;
+      int wtotal;
+      const int ex = wave_excl_scan(cnt, lane, &wtotal);
+      int base = 0;
+      if (lane == 0 && wtotal) base = atomicAdd(&s_count, wtotal);
+      base = __shfl(base, 0, 64) + ex;
+      while (word) {
+        la[base++] = t0 + (__builtin_ctz(word) >> 1);
+        word &= word - 1;
+      }
+    }
   }
   __syncthreads();
   int n = s_count;
@@ -83,24 +148,33 @@ __global__ __launch_bounds__(kNmsThreads) void nms_kernel(
       const int lo = t - g + 1 > 0 ? t - g + 1 : 0;
       const int hi = t + g - 1 < L - 1 ? t + g - 1 : L - 1;
       bool top = true;
-      for (int u = lo; u <= hi; ++u) {
-        if (u != t && st[u] != 0 && ranks_above(p[u], u, pt, t)) {
-          top = false;
-          break;
+      for (int wd = lo >> 4; wd <= (hi >> 4) && top; ++wd) {
+        uint32_t x = sw[wd] & range_fields(wd, lo, hi);
+        if (wd == (t >> 4)) x &= ~(3u << (2 * (t & 15)));
+        uint32_t nz = (x | (x >> 1)) & 0x55555555u;  // live or kept fields
+        while (nz) {
+          const int u = 16 * wd + (__builtin_ctz(nz) >> 1);
+          if (ranks_above(p[u], u, pt, t)) {
+            top = false;
+            break;
+          }
+          nz &= nz - 1;
         }
       }
-      if (top) st[t] = 2;
+      if (top) atomicXor(&sw[t >> 4], 3u << (2 * (t & 15)));  // live -> kept
     }
     __syncthreads();
-    // each candidate kept in this round retires the live ones near it (two
-    // kept candidates may share such a neighbour: both write the same 0)
+    // each candidate kept in this round retires the live ones near it
     for (int idx = tid; idx < n; idx += kNmsThreads) {
       const int t = la[idx];
-      if (st[t] != 2) continue;
+      if (field_of(sw, t) != 2u) continue;
       const int lo = t - g + 1 > 0 ? t - g + 1 : 0;
       const int hi = t + g - 1 < L - 1 ? t + g - 1 : L - 1;
-      for (int u = lo; u <= hi; ++u)
-        if (st[u] == 1) st[u] = 0;
+      for (int wd = lo >> 4; wd <= (hi >> 4); ++wd) {
+        const uint32_t x = sw[wd];
+        const uint32_t live = x & ~(x >> 1) & 0x55555555u & range_fields(wd, lo, hi);
+        if (live) atomicAnd(&sw[wd], ~(live | (live << 1)));
+      }
     }
     if (tid == 0) s_count = 0;
     __syncthreads();
@@ -111,12 +185,12 @@ __global__ __launch_bounds__(kNmsThreads) void nms_kernel(
       bool live = false;
       if (idx < n) {
         t = la[idx];
-        live = st[t] == 1;
+        live = field_of(sw, t) == 1u;
       }
       const uint64_t m = __ballot(live);
       int base = 0;
       if (lane == 0 && m) base = atomicAdd(&s_count, __popcll(m));
-      base = __shfl(base, 0);
+      base = __shfl(base, 0, 64);
       if (live) lb[base + __popcll(m & lanes_below(lane))] = t;
     }
     __syncthreads();
@@ -130,18 +204,23 @@ __global__ __launch_bounds__(kNmsThreads) void nms_kernel(
   // ---- kept tokens in token order -> offsets 0, kept..., L
   int32_t* out = offsets_out + (size_t)b * stride;
   int carry = 1;  // out[0] = 0
-  for (int t0 = 0; t0 < L; t0 += kNmsThreads) {
-    const int t = t0 + tid;
-    const bool kept = t < L && st[t] == 2;
-    const uint64_t m = __ballot(kept);
-    if (lane == 0) s_wsum[wv] = __popcll(m);
+  for (int w0 = 0; w0 < nw; w0 += kNmsThreads) {
+    const int w = w0 + tid;
+    uint32_t kept = w < nw ? (sw[w] >> 1) & 0x55555555u : 0u;
+    int wtotal;
+    const int ex = wave_excl_scan(__popc(kept), lane, &wtotal);
+    if (lane == 0) s_wsum[wv] = wtotal;
     __syncthreads();
     int before = carry, total = carry;
-    for (int w = 0; w < kNmsWaves; ++w) {
-      before += w < wv ? s_wsum[w] : 0;
-      total += s_wsum[w];
+    for (int x = 0; x < kNmsWaves; ++x) {
+      before += x < wv ? s_wsum[x] : 0;
+      total += s_wsum[x];
     }
-    if (kept) out[before + __popcll(m & lanes_below(lane))] = t;
+    int pos = before + ex;
+    while (kept) {
+      out[pos++] = 16 * w + (__builtin_ctz(kept) >> 1);
+      kept &= kept - 1;
+    }
     carry = total;
     __syncthreads();
   }
@@ -156,13 +235,10 @@ __global__ __launch_bounds__(kNmsThreads) void nms_kernel(
 
 hipError_t launch_nms(const float* scores, int32_t batch, int32_t seq_len, int32_t min_gap,
                       float threshold, int32_t* offsets_out, int32_t stride,
-                      int32_t* num_chunks_out, void* workspace, int64_t state_stride,
-                      hipStream_t stream) {
-  uint8_t* state = static_cast<uint8_t*>(workspace);
-  int32_t* lists = reinterpret_cast<int32_t*>(state + (size_t)batch * state_stride);
+                      int32_t* num_chunks_out, void* workspace, hipStream_t stream) {
   hipLaunchKernelGGL(nms_kernel, dim3(batch), dim3(kNmsThreads), 0, stream, scores, seq_len,
-                     min_gap, threshold, offsets_out, stride, num_chunks_out, state, lists,
-                     state_stride);
+                     min_gap, threshold, offsets_out, stride, num_chunks_out,
+                     static_cast<int32_t*>(workspace));
   return hipGetLastError();
 }
 

@@ -221,8 +221,10 @@ def test_nms_sizes():
     assert lib.dhsa_nms_offsets_stride(100, 0, ctypes.byref(st)) == ESHAPE
     n = ctypes.c_size_t()
     assert lib.dhsa_nms_workspace_size(2, 1000, 8, ctypes.byref(n)) == OK
-    assert n.value == 2 * 1024 + (2 * 2 * 1000 * 4 + 255) // 256 * 256
+    assert n.value == (2 * 2 * 1000 * 4 + 255) // 256 * 256
     assert lib.dhsa_nms_workspace_size(0, 1000, 8, ctypes.byref(n)) == ESHAPE
+    assert lib.dhsa_nms_workspace_size(1, 524288, 8, ctypes.byref(n)) == OK
+    assert lib.dhsa_nms_workspace_size(1, 524289, 8, ctypes.byref(n)) == EUNSUP
 
 
 @cpu_only
