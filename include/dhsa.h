@@ -263,7 +263,8 @@ int dhsa_layer_workspace_size(int32_t batch, int32_t seq_len, int32_t num_q_head
 
 /* One attention layer: dhsa_build_mask_ex then dhsa_sparse_prefill, run over
  * groups of consecutive sequences, each group as large as the workspace
- * allows (DHSA paper summary, Efficiency, "Batching": under a memory limit
+ * allows (gist.science Technical Summary, Experimental Results, Efficiency,
+ * "Batching": under a memory limit
  * the batch is processed sequence by sequence in a plain loop rather than
  * in one batched call).  Groups run in order on `stream` and reuse the one
  * workspace; results equal those of one pass over the whole batch.

@@ -1,8 +1,8 @@
 // One attention layer (mask construction + block-sparse attention) over a
 // batch of sequences, processed in groups of consecutive sequences that fit
 // a caller-given workspace.  A budget that holds one sequence's buffers gives
-// the sequential per-sequence loop (DHSA paper summary, Efficiency,
-// "Batching": in memory-constrained settings the batch is processed one
+// the sequential per-sequence loop (gist.science Technical Summary, Experimental Results,
+// Efficiency, "Batching": in memory-constrained settings the batch is processed one
 // sequence after another in a plain loop instead of one batched call);
 // a budget that holds every sequence gives one pass over the whole batch.
 // Host code only: each group is two calls of the C ABI on the caller's
