@@ -36,9 +36,10 @@
 //  * only the diagonal chunk needs the token-causal test (every earlier
 //    kept chunk lies entirely before the query chunk), and its key range is
 //    cut at the tile's last query row;
-//  * workgroups are renumbered so that each XCD (own L2) works on a
-//    contiguous range of (KV head, query tile) pairs, keeping one KV head's
-//    K/V hot in that XCD's L2.
+//  * workgroups are renumbered in runs of 32 consecutive (KV head, query
+//    tile, query head) items per XCD: a run keeps the query heads and tiles
+//    of one query chunk on one L2, and the eight XCDs advance through the
+//    list together, so they stream the K/V of the same KV head at a time.
 #include <float.h>
 
 #include "dhsa_internal.h"
@@ -57,6 +58,20 @@ constexpr int kTileElems = kBlockN * kHeadDim;  // one K or V sub-tile (bf16)
 constexpr int kTable = 512;                      // kept chunks per table window
 constexpr int kNumXcd = 8;
 constexpr float kLazyRescale = 8.0f;             // log2 of the largest p allowed
+
+// blocks of kXcdRun consecutive work items stay on one XCD (its L2 sees the
+// query heads and tiles of one query chunk together), and the XCDs advance
+// through the work list side by side, so at any time they all stream the K/V
+// of the same KV head (which then stays resident in the shared last-level
+// cache)
+constexpr int kXcdRun = 32;
+__device__ __forceinline__ int xcd_interleave(int w, int W) {
+  const int x = w % kNumXcd, k = w / kNumXcd;  // XCD and its k-th block
+  const int full = W / (kNumXcd * kXcdRun);    // complete rounds of runs
+  const int round = k / kXcdRun;
+  if (round < full) return (round * kNumXcd + x) * kXcdRun + (k % kXcdRun);
+  return w;  // the ragged last round keeps the dispatch order
+}
 
 __device__ __forceinline__ int xcd_remap(int w, int W) {
   const int q = W / kNumXcd, r = W % kNumXcd;
@@ -129,7 +144,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
   // ---- which (KV head, query tile, query head) this workgroup owns
   const int G = p.hq / p.hkv;
   const int W = p.num_tiles * p.hq;
-  const int w = xcd_remap((int)blockIdx.x, W);
+  const int w = p.order ? xcd_interleave((int)blockIdx.x, W) : xcd_remap((int)blockIdx.x, W);
   const int hg = w % G;
   const int rest = w / G;
   const int tile = rest % p.num_tiles;
