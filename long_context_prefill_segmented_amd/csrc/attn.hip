@@ -12,8 +12,11 @@
 // attention with variable-sized query and key blocks).
 //
 // Work decomposition (gfx950, wave64):
-//  * a workgroup = 4 waves = 128 query rows of ONE query chunk and ONE query
-//    head; each wave owns 32 rows; two workgroups share a CU;
+//  * a workgroup = NW waves = 32*NW query rows of ONE query chunk and ONE
+//    query head; each wave owns 32 rows.  Chunks are cut into tiles of 256
+//    rows (8 waves, one workgroup per CU) or 128 rows (4 waves, two per CU);
+//    a chunk's remainder of at most 32 rows goes to a second launch of one
+//    wave per workgroup with 32-key sub-tiles (four workgroups per CU);
 //  * the kept chunks of the row are concatenated into one gathered key
 //    stream (a prefix table in LDS maps stream positions to tokens), cut
 //    into 64-key sub-tiles that may cross chunk boundaries, so short chunks
@@ -115,10 +118,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-template <int NW>
+template <int NW, int KB>
 __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqTable st) {
   constexpr int kBlockM = 32 * NW;               // query rows per workgroup
-  constexpr int kRowsPerWave = kBlockN / NW;     // tile rows each wave loads
+  constexpr int kBN = 32 * KB;                   // keys per sub-tile
+  constexpr int kTileE = kBN * kHeadDim;         // one K or V sub-tile (bf16)
+  constexpr int kRowsPerWave = kBN / NW;         // tile rows each wave loads
   constexpr int kLoadsPerMat = kRowsPerWave / 4; // 1 KB direct loads per wave per matrix
   constexpr int kEntPerThread = kTable / (64 * NW);
   static_assert(kLoadsPerMat >= 1 && kEntPerThread >= 1, "shape");
@@ -126,10 +131,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
   // unrolled by two, so every access names its buffer statically and the
   // compiler can tell the in-flight direct loads into the other pair from
   // the reads of the current one (it does not wait for them)
-  __shared__ __attribute__((aligned(16))) uint16_t K0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t K1[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t V0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t V1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t K0[kTileE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[kTileE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[kTileE];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[kTileE];
   __shared__ int tbl_start[kTable];
   __shared__ int tbl_pref[kTable + 1];
   __shared__ int wsum[NW];
@@ -278,12 +283,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
     const int Gd0 = s_diag[0];
     const int Gd1 = s_diag[1];
     if (Gtot == 0) continue;
-    const int nsub = (Gtot + kBlockN - 1) / kBlockN;
+    const int nsub = (Gtot + kBN - 1) / kBN;
 
     Cursor cur{-1, 0, 0, 0};
     // direct-to-LDS loads of sub-tile js into (Kd, Vd)
     auto issue = [&](int js, uint16_t* Kd, uint16_t* Vd) {
-      const int pos = js * kBlockN + kRowsPerWave * wv + lwalk;
+      const int pos = js * kBN + kRowsPerWave * wv + lwalk;
       const int tok = pos < Gtot ? cursor_token(cur, pos, tbl_start, tbl_pref) : 0;
 #pragma unroll
       for (int u = 0; u < kLoadsPerMat; ++u) {
@@ -301,22 +306,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
     // one sub-tile js: compute on (Kt, Vt) while sub-tile js+1 streams into
     // (Kn, Vn), the buffers of sub-tile js-1
     auto subtile = [&](int js, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
-      const int p0 = js * kBlockN;
+      const int p0 = js * kBN;
       if (js + 1 < nsub) issue(js + 1, Kn, Vn);
       // a wave skips a sub-tile that lies inside the diagonal chunk beyond
       // all of its query rows
-      const bool skip = (p0 >= Gd0) && (p0 + kBlockN <= Gd1 || Gd1 >= Gtot) &&
+      const bool skip = (p0 >= Gd0) && (p0 + kBN <= Gd1 || Gd1 >= Gtot) &&
                         (p0 - Gd0 > qmin + 31);
       if (wave_active && !skip) {
         // ---- S^T = K Q^T, K operand reads one step ahead of the MFMAs
-        f32x16 sacc[2];
+        f32x16 sacc[KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) sacc[kb][rr] = 0.f;
-        bf16x8_t kcur[2], knext[2];
+        bf16x8_t kcur[KB], knext[KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
           const int row = kb * 32 + l32;
           kcur[kb] = *reinterpret_cast<const bf16x8_t*>(&Kt[row * kHeadDim + 8 * (hl ^ swz_k(row))]);
         }
@@ -324,18 +329,18 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
         for (int ds = 0; ds < 8; ++ds) {
           if (ds + 1 < 8) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
               const int row = kb * 32 + l32;
               knext[kb] = *reinterpret_cast<const bf16x8_t*>(
                   &Kt[row * kHeadDim + 8 * ((2 * ds + 2 + hl) ^ swz_k(row))]);
             }
           }
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < KB; ++kb)
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[kb], qf[ds], sacc[kb], 0, 0, 0);
           if (ds + 1 < 8) {
-            kcur[0] = knext[0];
-            kcur[1] = knext[1];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) kcur[kb] = knext[kb];
           }
         }
 
@@ -344,13 +349,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
         // (accumulator: lane -> query, register rr -> key
         //  8*(rr/4) + 4*(lane/32) + rr%4 of the 32-key block)
         const bool need_mask =
-            (p0 + kBlockN > Gtot) || (p0 + kBlockN > Gd0 + qmin + 1 && p0 < Gd1);
+            (p0 + kBN > Gtot) || (p0 + kBN > Gd0 + qmin + 1 && p0 < Gd1);
         if (need_mask) {
           const int rel_tot = Gtot - p0;
           const int rel_lo = Gd0 + qrow - p0;
           const int rel_hi = Gd1 - p0;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
               const int rel = kb * 32 + 8 * (rr >> 2) + 4 * hl + (rr & 3);
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[kb][rr]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -380,9 +385,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
         // values (the weights the PV product actually uses) two at a time
         const float mneg = m_run == -INFINITY ? 0.f : -m_run;
         const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-        bf16x2_t pp[2][8];
+        bf16x2_t pp[KB][8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float p0v = fast_exp2(__builtin_fmaf(sacc[kb][2 * e], c2, mneg));
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
         }
         // ---- O^T += V^T P^T
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const bf16x8_t pk = __builtin_shufflevector(
@@ -455,34 +460,54 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
   }
 }
 
-// One workgroup per sequence: expand chunk lengths into the query-tile list
-// (b, chunk, first row) with a block-wide exclusive scan.
+// One workgroup per sequence: expand chunk lengths into the query-tile lists
+// with block-wide exclusive scans.  A chunk gives floor(n / block_m) full
+// tiles of block_m rows; a remainder of more than kNarrowRows rows gives one
+// more tile of that list, a remainder of 1..kNarrowRows rows one tile of the
+// narrow list (32 rows, one wave).  Entries: (sequence, chunk, first row).
 __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restrict__ offs,
                                                          SeqTable st, int4* __restrict__ tiles,
+                                                         int4* __restrict__ narrow,
                                                          int32_t block_m) {
-  __shared__ int wsum[4];
+  __shared__ int wsum[2][4];
   const int b = blockIdx.x;
   const int C = st.num_chunks[b];
   const int obase = st.cbase[b] + b;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int base = st.tbase[b];
+  int base = st.tbase[b], nbase = st.ntbase[b];
   for (int c0 = 0; c0 < C; c0 += 256) {
     const int c = c0 + tid;
-    const int nt = c < C ? (offs[obase + c + 1] - offs[obase + c] + block_m - 1) / block_m : 0;
-    int incl = nt;
+    const int n = c < C ? offs[obase + c + 1] - offs[obase + c] : 0;
+    const int full = n / block_m, rem = n - full * block_m;
+    const int nt = full + (rem > kNarrowRows ? 1 : 0);
+    const int nn = (rem > 0 && rem <= kNarrowRows) ? 1 : 0;
+    int incl = nt, incn = nn;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
+      const int z = __shfl_up(incn, off, 64);
+      if (lane >= off) {
+        incl += y;
+        incn += z;
+      }
     }
-    if (lane == 63) wsum[wv] = incl;
+    if (lane == 63) {
+      wsum[0][wv] = incl;
+      wsum[1][wv] = incn;
+    }
     __syncthreads();
-    int pre = 0;
-    for (int x = 0; x < wv; ++x) pre += wsum[x];
-    const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    int pre = 0, pren = 0;
+    for (int x = 0; x < wv; ++x) {
+      pre += wsum[0][x];
+      pren += wsum[1][x];
+    }
+    const int tot = wsum[0][0] + wsum[0][1] + wsum[0][2] + wsum[0][3];
+    const int totn = wsum[1][0] + wsum[1][1] + wsum[1][2] + wsum[1][3];
     const int ex = base + pre + incl - nt;
     for (int t = 0; t < nt; ++t) tiles[ex + t] = make_int4(b, c, t * block_m, 0);
+    if (nn) narrow[nbase + pren + incn - nn] = make_int4(b, c, full * block_m, 0);
     base += tot;
+    nbase += totn;
     __syncthreads();
   }
 }
@@ -490,21 +515,37 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
 }  // namespace
 
 hipError_t launch_plan_tiles(const int32_t* offs_dev, const SeqTable& st, int4* tiles,
-                             int32_t block_m, hipStream_t stream) {
+                             int4* narrow, int32_t block_m, hipStream_t stream) {
   hipLaunchKernelGGL(plan_tiles_kernel, dim3(st.batch), dim3(256), 0, stream, offs_dev, st,
-                     tiles, block_m);
+                     tiles, narrow, block_m);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnParams& p, const SeqTable& st, hipStream_t stream) {
   const int64_t grid = (int64_t)p.num_tiles * p.hq;
-  if (grid <= 0) return hipSuccess;
-  if (p.block_m == kBlockMLarge) {
-    hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3((unsigned)grid), dim3(512), 0, stream, p, st);
-  } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, p, st);
+  if (grid > 0) {
+    if (p.block_m == kBlockMLarge) {
+      hipLaunchKernelGGL((attn_fwd_kernel<8, 2>), dim3((unsigned)grid), dim3(512), 0, stream, p,
+                         st);
+    } else {
+      hipLaunchKernelGGL((attn_fwd_kernel<4, 2>), dim3((unsigned)grid), dim3(256), 0, stream, p,
+                         st);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  // remainders of at most 32 rows: one wave per workgroup, 32-key sub-tiles
+  // (36 KB of LDS, so four such workgroups share a CU)
+  const int64_t ngrid = (int64_t)p.num_narrow * p.hq;
+  if (ngrid > 0) {
+    AttnParams q = p;
+    q.tiles = p.narrow;
+    q.num_tiles = p.num_narrow;
+    hipLaunchKernelGGL((attn_fwd_kernel<1, 1>), dim3((unsigned)ngrid), dim3(64), 0, stream, q,
+                       st);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace dhsa

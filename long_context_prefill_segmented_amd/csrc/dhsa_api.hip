@@ -121,16 +121,31 @@ int64_t score_tiles(int32_t batch, const int32_t* num_chunks, int32_t hq) {
   return t;
 }
 
+// Query tiles of one height: per chunk floor(n / block_m) full tiles plus
+// one for a remainder; with narrow != nullptr a remainder of at most
+// kNarrowRows rows is counted in *narrow instead (and its per-sequence base
+// written to nbase).
 int64_t query_tiles(int32_t batch, const int32_t* num_chunks, const int32_t* offs,
-                    int32_t block_m, int32_t* tbase) {
-  int64_t t = 0;
+                    int32_t block_m, int32_t* tbase, int64_t* narrow = nullptr,
+                    int32_t* nbase = nullptr) {
+  int64_t t = 0, nt = 0;
   size_t o = 0;
   for (int b = 0; b < batch; ++b) {
     if (tbase) tbase[b] = (int32_t)t;
-    for (int c = 0; c < num_chunks[b]; ++c)
-      t += (offs[o + c + 1] - offs[o + c] + block_m - 1) / block_m;
+    if (nbase) nbase[b] = (int32_t)nt;
+    for (int c = 0; c < num_chunks[b]; ++c) {
+      const int32_t n = offs[o + c + 1] - offs[o + c];
+      const int32_t full = n / block_m, rem = n - full * block_m;
+      if (narrow && rem > 0 && rem <= kNarrowRows) {
+        t += full;
+        nt += 1;
+      } else {
+        t += full + (rem > 0 ? 1 : 0);
+      }
+    }
     o += num_chunks[b] + 1;
   }
+  if (narrow) *narrow = nt;
   return t;
 }
 
@@ -144,13 +159,16 @@ int32_t choose_block_m(int32_t batch, const int32_t* num_chunks, const int32_t* 
     const int v = atoi(env);
     if (v == kBlockMSmall || v == kBlockMLarge) return v;
   }
+  // remainders of at most kNarrowRows rows go to the narrow tiles either way
   int64_t waves = 0, slots = 0;
   size_t o = 0;
   for (int b = 0; b < batch; ++b) {
     for (int c = 0; c < num_chunks[b]; ++c) {
       const int64_t n = offs[o + c + 1] - offs[o + c];
-      waves += (n + 31) / 32;
-      slots += (kBlockMLarge / 32) * ((n + kBlockMLarge - 1) / kBlockMLarge);
+      const int64_t full = n / kBlockMLarge, rem = n - full * kBlockMLarge;
+      const int64_t wide_rows = rem <= kNarrowRows ? full * kBlockMLarge : n;
+      waves += (wide_rows + 31) / 32;
+      slots += (kBlockMLarge / 32) * ((wide_rows + kBlockMLarge - 1) / kBlockMLarge);
     }
     o += num_chunks[b] + 1;
   }
@@ -459,11 +477,15 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
   if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale))
     return fail(DHSA_ERR_SHAPE, "softmax_scale is not finite");
   const int32_t ntiles_max = INT32_MAX / num_q_heads;
-  int32_t tbase[kMaxBatch];
+  int32_t tbase[kMaxBatch], nbase[kMaxBatch];
   const int32_t block_m = choose_block_m(batch, num_chunks, chunk_offsets);
-  const int64_t ntiles = query_tiles(batch, num_chunks, chunk_offsets, block_m, tbase);
-  if (ntiles > ntiles_max) return fail(DHSA_ERR_UNSUPPORTED, "too many query tiles");
-  const size_t need = align_up((size_t)ntiles * sizeof(int4));
+  int64_t nnarrow = 0;
+  const int64_t ntiles =
+      query_tiles(batch, num_chunks, chunk_offsets, block_m, tbase, &nnarrow, nbase);
+  if (ntiles > ntiles_max || nnarrow > ntiles_max)
+    return fail(DHSA_ERR_UNSUPPORTED, "too many query tiles");
+  // the workspace bound (tiles of the smaller height) also covers the two lists
+  const size_t need = align_up((size_t)(ntiles + nnarrow) * sizeof(int4));
   if (workspace_bytes < need)
     return fail(DHSA_ERR_CAPACITY, "workspace %zu < %zu bytes", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
@@ -471,10 +493,14 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
 
   SeqTable st;
   fill_table(st, batch, num_chunks, num_q_heads, 0);
-  for (int b = 0; b < batch; ++b) st.tbase[b] = tbase[b];
+  for (int b = 0; b < batch; ++b) {
+    st.tbase[b] = tbase[b];
+    st.ntbase[b] = nbase[b];
+  }
   hipStream_t strm = static_cast<hipStream_t>(stream);
   int4* tiles = static_cast<int4*>(workspace);
-  hipError_t e = launch_plan_tiles(chunk_offsets_dev, st, tiles, block_m, strm);
+  int4* narrow = tiles + ntiles;
+  hipError_t e = launch_plan_tiles(chunk_offsets_dev, st, tiles, narrow, block_m, strm);
   if (e != hipSuccess) return hip_fail(e, "tile plan launch");
 
   AttnParams p;
@@ -484,11 +510,13 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
   p.o = static_cast<uint16_t*>(out);
   p.lse = lse;
   p.tiles = tiles;
+  p.narrow = narrow;
   p.offs = chunk_offsets_dev;
   p.row_ptr = row_ptr;
   p.col_idx = col_idx;
   p.nnz = nnz;
   p.num_tiles = (int32_t)ntiles;
+  p.num_narrow = (int32_t)nnarrow;
   p.seq_len = seq_len;
   p.hq = num_q_heads;
   p.hkv = num_kv_heads;

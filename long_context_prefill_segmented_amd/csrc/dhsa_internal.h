@@ -28,6 +28,7 @@ struct SeqTable {
   int32_t num_chunks[kMaxBatch];
   int32_t cbase[kMaxBatch];    // sum of C over earlier sequences
   int32_t tbase[kMaxBatch];    // first query tile of the sequence
+  int32_t ntbase[kMaxBatch];   // first narrow query tile of the sequence
   int64_t sbase[kMaxBatch];    // first score element of the sequence
   int64_t nbase[kMaxBatch];    // first CSR entry of the sequence
 };
@@ -69,8 +70,11 @@ hipError_t launch_nms(const float* scores, int32_t batch, int32_t seq_len, int32
 int fail(int status, const char* fmt, ...);
 int ok();
 
+// query-tile remainders of at most this many rows go to the narrow list
+constexpr int kNarrowRows = 32;
+
 hipError_t launch_plan_tiles(const int32_t* offs_dev, const SeqTable& st,
-                             int4* tiles, int32_t block_m, hipStream_t stream);
+                             int4* tiles, int4* narrow, int32_t block_m, hipStream_t stream);
 
 struct AttnParams {
   const uint16_t* q;
@@ -79,11 +83,13 @@ struct AttnParams {
   uint16_t* o;
   float* lse;
   const int4* tiles;
+  const int4* narrow;  // tiles of at most kNarrowRows rows (one wave each)
   const int32_t* offs;
   const int32_t* row_ptr;
   const int32_t* col_idx;
   int64_t nnz;
   int32_t num_tiles;
+  int32_t num_narrow;
   int32_t seq_len;
   int32_t hq;
   int32_t hkv;
