@@ -199,6 +199,8 @@ int dhsa_build_mask_ex(const void* q, const void* k,
  *          [B][Hq][L].  A query with no visible key gets out = 0 and
  *          lse = -inf.
  * workspace: device, >= dhsa_prefill_workspace_size bytes.
+ * Limit: seq_len * num_kv_heads * 256 bytes (one sequence's K, or V) must
+ * stay below 4 GiB (DHSA_ERR_UNSUPPORTED otherwise).
  * The kernels bound-check CSR entries (entries outside [0, i] and row_ptr
  * values outside [0, nnz] are ignored), so a malformed CSR gives wrong
  * values but no out-of-bounds access. */

@@ -91,6 +91,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // LDS tile layout: element (row, d) of a [64][128] bf16 tile sits at
 //   row * 128 + 8 * (chunk ^ swz(row)) + d % 8,   chunk = d / 8,
 // with swz_k(row) = row & 15 for K and swz_v(row) = (row & 3) << 2 for V.
+// word 3 of a raw buffer descriptor (no swizzle, no index stride, 32-bit
+// data format) for the buffer loads below
+constexpr int kRsrcWord3 = 0x00020000;
+
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
 
@@ -118,7 +122,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-template <int NW, int KB>
+// PD: how many 16-dim steps ahead of its MFMA each K operand read is issued
+template <int NW, int KB, int PD>
 __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqTable st) {
   constexpr int kBlockM = 32 * NW;               // query rows per workgroup
   constexpr int kBN = 32 * KB;                   // keys per sub-tile
@@ -200,6 +205,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
   const size_t kv_rs = (size_t)p.hkv * kHeadDim;
   const char* kbytes = reinterpret_cast<const char*>(p.k + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim);
   const char* vbytes = reinterpret_cast<const char*>(p.v + (size_t)b * p.seq_len * kv_rs + (size_t)g * kHeadDim);
+  // buffer descriptors over this sequence's rows (the host keeps
+  // seq_len * rowbytes below 2^32).  The K/V tiles are staged with the
+  // buffer form of the direct-to-LDS load: while a global-form one is in
+  // flight the compiler can only wait for all LDS reads at once, which would
+  // serialise every K operand read below with its MFMA
+  const uint32_t nrec = (uint32_t)p.seq_len * rowbytes;
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbytes), 0, (int)nrec, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbytes), 0, (int)nrec, kRsrcWord3);
 
   // loader role: direct load u of wave wv fills tile rows
   // kRowsPerWave*wv + 4*u + lane/16, lane & 15 being the physical 16-byte
@@ -220,6 +235,34 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
   const int vd_off = 16 * (lgrp & 1) + 4 * (lsub & 3);
   const int qmin = q0 + wv * 32;  // first query row (chunk-local) of this wave
   constexpr int kNoDiag = 0x3fffffff;
+
+  bf16x2_t pp[KB][8];  // P^T of the current sub-tile, bf16 pairs
+  // ---- O^T += V^T P^T over the sub-tile whose V sits in Vs
+  auto pv = [&](const uint16_t* Vs) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8_t pk = __builtin_shufflevector(
+            __builtin_shufflevector(pp[kb][4 * hh], pp[kb][4 * hh + 1], 0, 1, 2, 3),
+            __builtin_shufflevector(pp[kb][4 * hh + 2], pp[kb][4 * hh + 3], 0, 1, 2, 3),
+            0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          bf16x4_t part[2];
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const int key = kb * 32 + 16 * hh + 8 * a + vkey_off;
+            const int d = db * 32 + vd_off;
+            const int idx = key * kHeadDim + 8 * ((d >> 3) ^ swz_v(key)) + (d & 7);
+            part[a] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DHSA_LDS bf16x4_t*)(&Vs[idx]));
+          }
+          const bf16x8_t va = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk, oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  };
 
   for (int64_t wb = e0; wb < e1; wb += kTable) {
     const int nent = (int)((e1 - wb) < kTable ? (e1 - wb) : kTable);
@@ -296,10 +339,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
         const uint32_t rb = tk * rowbytes;
         uint16_t* kd = Kd + (kRowsPerWave * wv + 4 * u) * kHeadDim;
         uint16_t* vd = Vd + (kRowsPerWave * wv + 4 * u) * kHeadDim;
-        __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)(kbytes + (rb + kchunk[u])),
-                                         (DHSA_LDS void*)kd, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const DHSA_GLOBAL void*)(vbytes + (rb + vchunk)),
-                                         (DHSA_LDS void*)vd, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (DHSA_LDS void*)kd, 16, (int)(rb + kchunk[u]),
+                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (DHSA_LDS void*)vd, 16, (int)(rb + vchunk), 0,
+                                                 0, 0);
       }
     };
 
@@ -319,30 +362,31 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) sacc[kb][rr] = 0.f;
-        bf16x8_t kcur[KB], knext[KB];
+        // operand ring: step ds lives in slot ds % PD, read PD steps ahead
+        bf16x8_t kr[PD][KB];
+        auto ld = [&](int ds, int slot) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int row = kb * 32 + l32;
-          kcur[kb] = *reinterpret_cast<const bf16x8_t*>(&Kt[row * kHeadDim + 8 * (hl ^ swz_k(row))]);
-        }
+          for (int kb = 0; kb < KB; ++kb) {
+            const int row = kb * 32 + l32;
+            kr[slot][kb] = *reinterpret_cast<const bf16x8_t*>(
+                &Kt[row * kHeadDim + 8 * ((2 * ds + hl) ^ swz_k(row))]);
+          }
+        };
+#pragma unroll
+        for (int ds = 0; ds < PD; ++ds) ld(ds, ds);
 #pragma unroll
         for (int ds = 0; ds < 8; ++ds) {
-          if (ds + 1 < 8) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              const int row = kb * 32 + l32;
-              knext[kb] = *reinterpret_cast<const bf16x8_t*>(
-                  &Kt[row * kHeadDim + 8 * ((2 * ds + 2 + hl) ^ swz_k(row))]);
-            }
-          }
+          const int slot = ds % PD;
+          // keep the ring as written: the scheduler would otherwise pull each
+          // read down to just before its MFMA
+          if (PD > 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[kb], qf[ds], sacc[kb], 0, 0, 0);
-          if (ds + 1 < 8) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) kcur[kb] = knext[kb];
-          }
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[slot][kb], qf[ds], sacc[kb], 0, 0,
+                                                               0);
+          if (ds + PD < 8) ld(ds + PD, slot);
         }
+        if (PD > 2) __builtin_amdgcn_sched_barrier(0);
 
         // ---- mask: only the tail of the stream and the part of the diagonal
         // chunk past this wave's first query row can hold hidden keys
@@ -385,7 +429,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
         // values (the weights the PV product actually uses) two at a time
         const float mneg = m_run == -INFINITY ? 0.f : -m_run;
         const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-        bf16x2_t pp[KB][8];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -396,30 +439,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
             l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[kb][e], ones, l_run, false);
           }
         }
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const bf16x8_t pk = __builtin_shufflevector(
-                __builtin_shufflevector(pp[kb][4 * hh], pp[kb][4 * hh + 1], 0, 1, 2, 3),
-                __builtin_shufflevector(pp[kb][4 * hh + 2], pp[kb][4 * hh + 3], 0, 1, 2, 3),
-                0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              bf16x4_t part[2];
-#pragma unroll
-              for (int a = 0; a < 2; ++a) {
-                const int key = kb * 32 + 16 * hh + 8 * a + vkey_off;
-                const int d = db * 32 + vd_off;
-                const int idx = key * kHeadDim + 8 * ((d >> 3) ^ swz_v(key)) + (d & 7);
-                part[a] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DHSA_LDS bf16x4_t*)(&Vt[idx]));
-              }
-              const bf16x8_t va = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk, oacc[db], 0, 0, 0);
-            }
-          }
-        }
+        pv(Vt);
       }
       wait_vmcnt<0>();  // this wave's loads of sub-tile js+1 have landed
       __syncthreads();
@@ -525,11 +545,11 @@ hipError_t launch_attention(const AttnParams& p, const SeqTable& st, hipStream_t
   const int64_t grid = (int64_t)p.num_tiles * p.hq;
   if (grid > 0) {
     if (p.block_m == kBlockMLarge) {
-      hipLaunchKernelGGL((attn_fwd_kernel<8, 2>), dim3((unsigned)grid), dim3(512), 0, stream, p,
+      hipLaunchKernelGGL((attn_fwd_kernel<8, 2, 3>), dim3((unsigned)grid), dim3(512), 0, stream, p,
                          st);
     } else {
-      hipLaunchKernelGGL((attn_fwd_kernel<4, 2>), dim3((unsigned)grid), dim3(256), 0, stream, p,
-                         st);
+      hipLaunchKernelGGL((attn_fwd_kernel<4, 2, 2>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, p, st);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -541,8 +561,8 @@ hipError_t launch_attention(const AttnParams& p, const SeqTable& st, hipStream_t
     AttnParams q = p;
     q.tiles = p.narrow;
     q.num_tiles = p.num_narrow;
-    hipLaunchKernelGGL((attn_fwd_kernel<1, 1>), dim3((unsigned)ngrid), dim3(64), 0, stream, q,
-                       st);
+    hipLaunchKernelGGL((attn_fwd_kernel<1, 1, 2>), dim3((unsigned)ngrid), dim3(64), 0,
+                       stream, q, st);
     return hipGetLastError();
   }
   return hipSuccess;

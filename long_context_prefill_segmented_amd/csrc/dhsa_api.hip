@@ -476,6 +476,10 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
   if (s) return s;
   if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale))
     return fail(DHSA_ERR_SHAPE, "softmax_scale is not finite");
+  // the attention kernel addresses a sequence's K/V rows with 32-bit offsets
+  if ((uint64_t)seq_len * num_kv_heads * kHeadDim * 2 > UINT32_MAX)
+    return fail(DHSA_ERR_UNSUPPORTED, "seq_len * num_kv_heads * %d bytes exceeds 4 GiB",
+                kHeadDim * 2);
   const int32_t ntiles_max = INT32_MAX / num_q_heads;
   int32_t tbase[kMaxBatch], nbase[kMaxBatch];
   const int32_t block_m = choose_block_m(batch, num_chunks, chunk_offsets);

@@ -155,6 +155,11 @@ def test_sparse_prefill_rejects_bad_arguments():
     assert _prefill(scale=float("nan")) == ESHAPE
     assert _prefill(scale=float("inf")) == ESHAPE
     assert _prefill(ws_bytes=8) == ECAP
+    # one sequence's K (or V) must stay below 4 GiB: 2^20 tokens x 16 KV heads x 256 B = 4 GiB
+    L = 1 << 20
+    assert _prefill(seq_len=L, hq=16, hkv=16, nc=[1], offs=[0, L]) == EUNSUP
+    assert b"4 GiB" in lib.dhsa_last_error()
+    assert _prefill(seq_len=L, hq=16, hkv=8, nc=[1], offs=[0, L], ws_bytes=8) == ECAP
 
 
 @cpu_only
