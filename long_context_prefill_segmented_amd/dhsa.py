@@ -29,6 +29,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is not built; run `python -m long_context_prefill_segmented_amd.build_lib`")
 
+# limits of include/dhsa.h (the same #defines; a CPU test keeps them equal)
+HEAD_DIM = 128
+MAX_BATCH = 64
+MAX_CHUNKS = 2048
+NMS_MAX_LEN = 524288
+
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t

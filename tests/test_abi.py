@@ -40,6 +40,13 @@ def test_every_declared_function_is_exported():
     assert declared == set(dhsa.EXPORTED)
 
 
+def test_binding_limits_match_the_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"^#define DHSA_(\w+) (\d+)", text, re.M))
+    for name in ("HEAD_DIM", "MAX_BATCH", "MAX_CHUNKS", "NMS_MAX_LEN"):
+        assert int(defs[name]) == getattr(dhsa, name), name
+
+
 def test_status_strings_and_version():
     assert lib.dhsa_status_string(0) == b"DHSA_OK"
     assert lib.dhsa_status_string(EOFF) == b"DHSA_ERR_OFFSETS"

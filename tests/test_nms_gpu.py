@@ -80,6 +80,18 @@ def test_nms_monotone_ramps_and_degenerate_cases():
     run_and_compare(np.ones((1, 1), np.float32), 1, 0.5, "one token")
 
 
+def test_nms_at_the_maximum_length():
+    # DHSA_NMS_MAX_LEN tokens: every 2-bit token state of the sequence in LDS
+    L = dhsa.NMS_MAX_LEN
+    offsets = [synth.draw_chunk_lengths(np.random.default_rng(6), L, ((1.0, 64, 512),))]
+    p = synth.boundary_scores(offsets, L, seed=10)
+    out = run_and_compare(p, 32, 0.5, "maximum length")
+    assert len(out[0]) > 1000
+    # dense candidates at that length (one in four tokens above threshold)
+    p = np.random.default_rng(7).random((1, L), dtype=np.float32)
+    run_and_compare(p, 8, 0.75, "maximum length, dense")
+
+
 def test_nms_reuse_and_smaller_batch():
     # one BoundaryNMS object, two different inputs: no state leaks between calls
     rng = np.random.default_rng(5)

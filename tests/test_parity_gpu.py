@@ -54,6 +54,10 @@ CASES = {
     # more than 1024 chunks per sequence (17 candidate slots per lane)
     "many_chunks": synth.small_workload("many_chunks", 1, 4096, 2, 1, (1, 4), "iid", topk=8,
                                         seed=37),
+    # exactly DHSA_MAX_CHUNKS chunks (one token each): the largest selection
+    # a sequence may ask for, 32 candidate slots per lane
+    "max_chunks": synth.small_workload("max_chunks", 1, 2048, 2, 1, (1, 1), "iid", topk=5,
+                                       seed=39),
 }
 
 _cache = {}
@@ -172,7 +176,8 @@ def test_chunk_score_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "mha_dense",
-                                  "topk1", "unit_chunks", "many_entries"])
+                                  "topk1", "unit_chunks", "many_entries", "many_chunks",
+                                  "max_chunks"])
 def test_topk_bit_exact_on_oracle_scores(name):
     c = get_case(name)
     flat = np.concatenate([r["s32"].reshape(-1) for r in c.ref]).astype(np.float32)
