@@ -201,6 +201,10 @@ int dhsa_build_mask_ex(const void* q, const void* k,
  * workspace: device, >= dhsa_prefill_workspace_size bytes.
  * Limit: seq_len * num_kv_heads * 256 bytes (one sequence's K, or V) must
  * stay below 4 GiB (DHSA_ERR_UNSUPPORTED otherwise).
+ * Query tiles are 256 rows when at least 75 % of their 32-row slots hold
+ * rows, else 128; chunk remainders of at most 32 rows run in one-wave tiles.
+ * The environment variable DHSA_ATTN_BLOCK_M=128 or 256 forces the height
+ * (results are the same up to floating-point summation order).
  * The kernels bound-check CSR entries (entries outside [0, i] and row_ptr
  * values outside [0, nnz] are ignored), so a malformed CSR gives wrong
  * values but no out-of-bounds access. */

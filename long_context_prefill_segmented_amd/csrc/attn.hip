@@ -76,12 +76,6 @@ __device__ __forceinline__ int xcd_interleave(int w, int W) {
   return w;  // the ragged last round keeps the dispatch order
 }
 
-__device__ __forceinline__ int xcd_remap(int w, int W) {
-  const int q = W / kNumXcd, r = W % kNumXcd;
-  const int x = w % kNumXcd, idx = w / kNumXcd;
-  return x < r ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
-}
-
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
@@ -154,7 +148,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
   // ---- which (KV head, query tile, query head) this workgroup owns
   const int G = p.hq / p.hkv;
   const int W = p.num_tiles * p.hq;
-  const int w = p.order ? xcd_interleave((int)blockIdx.x, W) : xcd_remap((int)blockIdx.x, W);
+  const int w = xcd_interleave((int)blockIdx.x, W);
   const int hg = w % G;
   const int rest = w / G;
   const int tile = rest % p.num_tiles;

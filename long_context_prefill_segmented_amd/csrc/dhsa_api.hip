@@ -525,11 +525,6 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
   p.hq = num_q_heads;
   p.hkv = num_kv_heads;
   p.block_m = block_m;
-  {
-    // DHSA_ATTN_ORDER=0 restores one XCD per KV-head range
-    const char* oenv = getenv("DHSA_ATTN_ORDER");
-    p.order = oenv ? atoi(oenv) : 1;
-  }
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kHeadDim);
   p.scale_log2 = scale * 1.4426950408889634f;
   e = launch_attention(p, st, strm);

@@ -94,7 +94,6 @@ struct AttnParams {
   int32_t hq;
   int32_t hkv;
   int32_t block_m;  // query tile height: kBlockMSmall or kBlockMLarge
-  int32_t order;    // workgroup order: 0 = one XCD per KV-head range, 1 = interleaved
   float scale_log2;
 };
 
