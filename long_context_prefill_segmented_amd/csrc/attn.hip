@@ -542,7 +542,7 @@ hipError_t launch_attention(const AttnParams& p, const SeqTable& st, hipStream_t
       hipLaunchKernelGGL((attn_fwd_kernel<8, 2, 3>), dim3((unsigned)grid), dim3(512), 0, stream, p,
                          st);
     } else {
-      hipLaunchKernelGGL((attn_fwd_kernel<4, 2, 2>), dim3((unsigned)grid), dim3(256), 0,
+      hipLaunchKernelGGL((attn_fwd_kernel<4, 2, 3>), dim3((unsigned)grid), dim3(256), 0,
                          stream, p, st);
     }
     const hipError_t e = hipGetLastError();
