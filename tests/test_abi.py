@@ -47,6 +47,32 @@ def test_binding_limits_match_the_header():
         assert int(defs[name]) == getattr(dhsa, name), name
 
 
+def test_error_messages_are_per_thread():
+    import threading
+    seen = {}
+
+    def worker(name, topk, recent):
+        nc = _arr([4])
+        msgs = set()
+        for _ in range(200):
+            st = lib.dhsa_csr_capacity(1, nc.ctypes.data, 2, topk, recent,
+                                       ctypes.byref(ctypes.c_int32()),
+                                       ctypes.byref(ctypes.c_int64()))
+            msgs.add((st, lib.dhsa_last_error()))
+        seen[name] = msgs
+
+    ts = [threading.Thread(target=worker, args=("topk", 0, 0)),
+          threading.Thread(target=worker, args=("recent", 2, -1)),
+          threading.Thread(target=worker, args=("ok", 2, 1))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert seen["topk"] == {(ETOPK, b"topk 0 < 1")}
+    assert seen["recent"] == {(ETOPK, b"recent -1 < 0")}
+    assert seen["ok"] == {(OK, b"")}
+
+
 def test_status_strings_and_version():
     assert lib.dhsa_status_string(0) == b"DHSA_OK"
     assert lib.dhsa_status_string(EOFF) == b"DHSA_ERR_OFFSETS"
