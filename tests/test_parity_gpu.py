@@ -58,6 +58,11 @@ CASES = {
     # a sequence may ask for, 32 candidate slots per lane
     "max_chunks": synth.small_workload("max_chunks", 1, 2048, 2, 1, (1, 1), "iid", topk=5,
                                        seed=39),
+    # 16 query heads per KV head
+    "gqa16": synth.small_workload("gqa16", 1, 2048, 16, 1, (32, 300), "iid", topk=4, seed=43),
+    # five sequences with different chunk counts and lengths
+    "batch5": synth.small_workload("batch5", 5, 1536, 4, 2,
+                                   ((0.6, 8, 64), (0.4, 100, 400)), "iid", topk=4, seed=44),
 }
 
 _cache = {}
@@ -132,7 +137,8 @@ def assert_attention_close(gpu, ref, what):
 # ---------------------------------------------------------------- stages
 
 
-@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "unit_chunks"])
+@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "unit_chunks",
+                                  "gqa16", "batch5"])
 def test_pool_parity(name):
     c = get_case(name)
     for which, t, bits, H in (("q", c.q, c.x.q, c.hq), ("k", c.k, c.x.k, c.hkv)):
@@ -155,7 +161,7 @@ def test_pool_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "many_entries",
-                                  "many_chunks"])
+                                  "many_chunks", "gqa16", "batch5"])
 def test_chunk_score_parity(name):
     c = get_case(name)
     say("  build_mask with scores")
@@ -177,7 +183,7 @@ def test_chunk_score_parity(name):
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "mha_dense",
                                   "topk1", "unit_chunks", "many_entries", "many_chunks",
-                                  "max_chunks"])
+                                  "max_chunks", "gqa16", "batch5"])
 def test_topk_bit_exact_on_oracle_scores(name):
     c = get_case(name)
     flat = np.concatenate([r["s32"].reshape(-1) for r in c.ref]).astype(np.float32)
@@ -231,7 +237,7 @@ def test_topk_ties_and_signed_zero():
 
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "topk1",
-                                  "many_chunks"])
+                                  "many_chunks", "gqa16", "batch5"])
 def test_build_mask_matches_oracle_mask(name):
     c = get_case(name)
     csr = dhsa.build_mask(c.q, c.k, c.offs, c.topk)
@@ -287,7 +293,7 @@ def test_attention_on_oracle_mask(name, block_m):
     assert np.all(np.abs(lg - lse_ref) <= LSE_TOL * (1 + np.abs(lse_ref)))
 
 
-@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured"])
+@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "gqa16", "batch5"])
 def test_attention_on_gpu_mask_end_to_end(name, block_m):
     c = get_case(name)
     csr = dhsa.build_mask(c.q, c.k, c.offs, c.topk)
