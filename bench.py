@@ -207,6 +207,50 @@ def time_batched_loop(dhsa, synth, torch, dev, name="ragged_2x64k", steps=5):
     return res
 
 
+def measure_ceilings(torch, dev, reps=10):
+    """On-box references, timed outside the layer's timed region with torch as
+    a measuring tool: bf16 GEMMs of 8192^3 and 16384^3 (torch.matmul on
+    contiguous 2-D operands, the faster reported) as the reachable MFMA
+    rate, plus torch's 2 GiB device copy (read + write bytes) and its sum
+    over 4 GiB of fp32 (read bytes) as memory references."""
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms
+
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    copy_ms = timed(lambda: b.copy_(a))
+    del a, b
+    f = torch.ones(n // 2, dtype=torch.float32, device=dev)  # 4 GiB
+    read_ms = timed(lambda: f.sum())
+    del f
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    gemm = {}
+    for m in (8192, 16384):
+        x = torch.randn(m, m, dtype=torch.bfloat16, device=dev, generator=g)
+        y = torch.randn(m, m, dtype=torch.bfloat16, device=dev, generator=g)
+        gemm[m] = 2 * m ** 3 / (timed(lambda: torch.matmul(x, y)) * 1e-3) / 1e12
+        del x, y
+    torch.cuda.empty_cache()
+    return {"torch_copy_GBps": 2 * n / (copy_ms * 1e-3) / 1e9,
+            "torch_sum_read_GBps": 2 * n / (read_ms * 1e-3) / 1e9,
+            "bf16_gemm_TFLOPs": max(gemm.values()),
+            "bf16_gemm_TFLOPs_by_size": {str(m): v for m, v in gemm.items()},
+            "how": "2 GiB device copy (read + write bytes), sum of 4 GiB fp32 (read bytes), "
+                   f"8192^3 and 16384^3 bf16 matmuls; {reps} repetitions each, outside the "
+                   "timed region"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,7 +259,8 @@ def main():
     ap.add_argument("--workload", default="llama31_8b_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the per-row-budget + recent-window selection leg")
+                    help="skip the widened-selection, NMS and batched-loop legs and the "
+                         "reference ceilings (for profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -300,6 +345,16 @@ def main():
         variants["boundary_nms"] = time_nms(dhsa, synth, torch, x, dev)
         variants["batched_loop"] = time_batched_loop(dhsa, synth, torch, dev)
 
+    ceilings = None
+    if not args.no_variants:
+        log("[bench] reference ceilings (copy, bf16 GEMM)")
+        ceilings = measure_ceilings(torch, dev)
+        # torch's copy and reduction are references, not the HBM limit (the
+        # pooling kernel streams faster than either)
+        ceilings["mask_vs_torch_copy"] = (mask_bytes / (mask_avg * 1e-3) / 1e9) / \
+            ceilings["torch_copy_GBps"]
+        ceilings["attention_frac_of_gemm"] = achieved / ceilings["bf16_gemm_TFLOPs"]
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
@@ -323,6 +378,8 @@ def main():
                    "num_chunks": [len(o) - 1 for o in x.offsets], "nnz": int(ci.size)},
         "mask_ms": mask_avg,
         "attention_ms": attn_avg,
+        "mask_ms_median": statistics.median(mask_ms),
+        "attention_ms_median": statistics.median(attn_ms),
         "mask_GBps": mask_bytes / (mask_avg * 1e-3) / 1e9,
         "mask_hbm_frac": mask_bytes / (mask_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "kept_tile_TFLOP": flops / 1e12,
@@ -330,6 +387,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic},
+        "ceilings": ceilings,
         "variants": variants,
         "cpu_baseline": cpu,
     }
