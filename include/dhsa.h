@@ -203,8 +203,11 @@ int dhsa_build_mask_ex(const void* q, const void* k,
  * stay below 4 GiB (DHSA_ERR_UNSUPPORTED otherwise).
  * Query tiles are 256 rows when at least 75 % of their 32-row slots hold
  * rows, else 128; chunk remainders of at most 32 rows run in one-wave tiles.
- * The environment variable DHSA_ATTN_BLOCK_M=128 or 256 forces the height
- * (results are the same up to floating-point summation order).
+ * The environment variable DHSA_ATTN_BLOCK_M=128 or 256 forces the height.
+ * Results of the two heights agree to rounding: a row whose tile changes
+ * between a wide kernel and the one-wave kernel sees 32-key instead of
+ * 64-key key blocks, so its running softmax maximum is refreshed at other
+ * points.
  * The kernels bound-check CSR entries (entries outside [0, i] and row_ptr
  * values outside [0, nnz] are ignored), so a malformed CSR gives wrong
  * values but no out-of-bounds access. */
