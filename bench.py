@@ -8,7 +8,15 @@ HBM.  Prints ONE JSON line:
   value        kept-tile TFLOP/s over the whole layer (mask + attention)
   ms_per_step  ms per layer
   roofline     the attention kernel against the bf16 MFMA peak
+  mask_stages  pooling, chunk scores and top-k timed one by one (stage calls),
+               with the HBM GB/s of pooling and top-k
+  layers       the other layer shapes (Qwen2.5-3B at 16K, Llama-3.1-8B at
+               32K) and the same 128K layer with every causal chunk kept
+               (dense causal, the sparse-vs-dense context), each as ms per
+               layer, kept-tile TFLOP/s and mask GB/s against the roofline
   cpu_baseline the CPU oracle on a bounded sample of the same layer
+Latencies are also given as the median of 5 timed runs after 2 warmups (the
+DHSA README's kernel-latency protocol) next to the mean over --steps runs.
 """
 from __future__ import annotations
 
@@ -63,36 +71,57 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(x, rows_gpu_unused, hq, hkv, budget_rows=1500, seed=0):
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, hq, hkv, budget_rows=1500, seed=0):
     """The oracle, untuned, on a bounded sample of the layer: full-layer mask
     construction plus attention for a seeded sample of (head, query chunk)
-    rows, scaled to kept-tile TFLOP/s."""
+    rows, scaled to kept-tile TFLOP/s.  Runs on every core this process may
+    use (its CPU affinity set), with the BLAS thread pools pinned to that
+    count."""
     from oracle import dhsa_oracle as orc
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
-        cores = 1
-    b = 0
-    t0 = time.perf_counter()
-    q = orc.widen_bf16(x.q[b])
-    k = orc.widen_bf16(x.k[b])
-    _, _, _, _, rows = orc.build_mask(q, k, x.offsets[b], x.topk)
-    t_mask = time.perf_counter() - t0
-    v = orc.widen_bf16(x.v[b])
-    rng = np.random.default_rng(seed)
-    o = np.asarray(x.offsets[b], dtype=np.int64)
-    C = o.size - 1
-    n = np.diff(o)
-    G = hq // hkv
-    picks = [(int(rng.integers(0, hq)), int(rng.integers(0, C))) for _ in range(budget_rows)]
-    flops = 0
-    t1 = time.perf_counter()
-    for (h, i) in picks:
-        orc.chunk_attention(q, k, v, o, rows[h][i], i, h, h // G, 1.0 / math.sqrt(128))
-        cols = np.asarray(rows[h][i])
-        flops += 4 * 128 * (int(n[i]) * int(n[cols[cols < i]].sum()) + int(n[i]) * (int(n[i]) + 1) // 2)
-    t_att = time.perf_counter() - t1
+        threadpool_info, limiter = None, None
+    try:
+        blas = sorted({i.get("num_threads", 1) for i in threadpool_info()}) if threadpool_info \
+            else []
+        b = 0
+        t0 = time.perf_counter()
+        q = orc.widen_bf16(x.q[b])
+        k = orc.widen_bf16(x.k[b])
+        _, _, _, _, rows = orc.build_mask(q, k, x.offsets[b], x.topk)
+        t_mask = time.perf_counter() - t0
+        v = orc.widen_bf16(x.v[b])
+        rng = np.random.default_rng(seed)
+        o = np.asarray(x.offsets[b], dtype=np.int64)
+        C = o.size - 1
+        n = np.diff(o)
+        G = hq // hkv
+        picks = [(int(rng.integers(0, hq)), int(rng.integers(0, C))) for _ in range(budget_rows)]
+        flops = 0
+        t1 = time.perf_counter()
+        for (h, i) in picks:
+            orc.chunk_attention(q, k, v, o, rows[h][i], i, h, h // G, 1.0 / math.sqrt(128))
+            cols = np.asarray(rows[h][i])
+            flops += 4 * 128 * (int(n[i]) * int(n[cols[cols < i]].sum())
+                                + int(n[i]) * (int(n[i]) + 1) // 2)
+        t_att = time.perf_counter() - t1
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
     rows_total = hq * C * x.workload.batch
     frac = budget_rows / rows_total
     t_layer_share = t_att + t_mask * frac
@@ -101,10 +130,144 @@ def cpu_baseline(x, rows_gpu_unused, hq, hkv, budget_rows=1500, seed=0):
         "unit": "TFLOP/s (kept tiles)",
         "cores": int(cores),
         "kind": "oracle",
+        "cpu_model": host_cpu_model(),
+        "blas_threads": blas,
         "sample": (f"oracle (NumPy float64) mask construction of the whole layer ({t_mask:.1f} s, "
                    f"prorated by {frac:.2e}) + attention of {budget_rows} seeded (head, query "
-                   f"chunk) rows ({t_att:.1f} s, {flops / 1e9:.1f} GFLOP kept)"),
+                   f"chunk) rows ({t_att:.1f} s, {flops / 1e9:.1f} GFLOP kept); cores = the "
+                   f"process's CPU affinity set, BLAS pools limited to it"),
     }
+
+
+def mask_bytes_of(w, hq, hkv, rp_size, nnz):
+    """Algorithmic bytes of mask construction: Q and K read once, the CSR
+    written once (pooled vectors and scores stay in the L2-sized workspace
+    and are not counted)."""
+    return 2 * w.batch * w.seq_len * (hq + hkv) * 128 + 4 * (rp_size + nnz)
+
+
+def timed_runs(torch, stream, fns, steps):
+    """Runs the callables in order `steps` times, with HIP events recorded on
+    `stream` around each; returns per-callable lists of ms."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+          for _ in range(steps)]
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for j, f in enumerate(fns):
+            f()
+            ev[s][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return [[ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)]
+            for j in range(len(fns))]
+
+
+def pages_protocol(torch, stream, fns, warmup=2, timed=5):
+    """The DHSA README's kernel-latency protocol: `warmup` untimed runs, then
+    the median of `timed` runs (per callable, ms)."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return [statistics.median(t) for t in timed_runs(torch, stream, fns, timed)]
+
+
+def time_layer(dhsa, synth, torch, dev, name, steps, topk=None, label=None, x=None):
+    """One whole layer (mask + attention) of workload `name`, inputs resident:
+    mean over `steps` runs and the median of 5 after 2 warmups.  topk
+    overrides the workload's (topk >= the chunk count keeps every causal
+    chunk: dense causal attention through the same kernels)."""
+    w = synth.WORKLOADS[name]
+    if x is None:
+        x = synth.generate(w)
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    k_used = x.topk if topk is None else topk
+    offs = dhsa.ChunkOffsets.from_list(x.offsets, w.seq_len, device=dev)
+    q, k, v = (dhsa.bf16_from_bits(a, dev) for a in (x.q, x.k, x.v))
+    mb = dhsa.MaskBuilder(offs, hq, hkv, k_used, device=dev)
+    pf = dhsa.Prefill(offs, hq, hkv, device=dev)
+    stream = torch.cuda.current_stream()
+    state = {}
+
+    def mask():
+        state["csr"] = mb(q, k)
+
+    def attn():
+        pf(q, k, v, state["csr"])
+
+    p_mask, p_attn = pages_protocol(torch, stream, [mask, attn])
+    rp = state["csr"].row_ptr.cpu().numpy()
+    ci = state["csr"].col_idx.cpu().numpy()[:state["csr"].nnz]
+    flops = kept_tile_flops(x.offsets, rp, ci, hq)
+    t_mask, t_attn = timed_runs(torch, stream, [mask, attn], steps)
+    m_avg, a_avg = statistics.mean(t_mask), statistics.mean(t_attn)
+    mbytes = mask_bytes_of(w, hq, hkv, rp.size, ci.size)
+    res = {
+        "workload": label or name, "batch": w.batch, "seq_len": w.seq_len,
+        "num_q_heads": hq, "num_kv_heads": hkv, "topk": k_used,
+        "num_chunks": [len(o) - 1 for o in x.offsets], "nnz": int(ci.size),
+        "chunk_pair_density": float(ci.size / (hq * sum((len(o) - 1) * len(o) // 2
+                                                          for o in x.offsets))),
+        "steps": steps, "ms_per_layer": m_avg + a_avg, "mask_ms": m_avg, "attention_ms": a_avg,
+        "ms_per_layer_median5": p_mask + p_attn, "mask_ms_median5": p_mask,
+        "attention_ms_median5": p_attn,
+        "kept_tile_TFLOP": flops / 1e12,
+        "TFLOP_per_s": flops / ((m_avg + a_avg) * 1e-3) / 1e12,
+        "attention_TFLOP_per_s": flops / (a_avg * 1e-3) / 1e12,
+        "attention_frac_of_peak": flops / (a_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "mask_GBps": mbytes / (m_avg * 1e-3) / 1e9,
+        "mask_frac_of_hbm": mbytes / (m_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+    }
+    log(f"[bench] layer {res['workload']}: mask {m_avg:.3f} ms  attention {a_avg:.3f} ms  "
+        f"({res['attention_TFLOP_per_s']:.0f} TFLOP/s, mask {res['mask_GBps']:.0f} GB/s)")
+    del q, k, v, mb, pf, state
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_mask_stages(dhsa, torch, x, offs, q, k, hq, hkv, steps):
+    """The mask's steps one at a time through the stage calls, into
+    preallocated buffers: pooling of Q and of K (dhsa_pool), chunk scores
+    (dhsa_chunk_scores), causal top-k to CSR (dhsa_topk_csr).  GB/s are
+    algorithmic bytes: pooling reads the tensor once and writes the pooled
+    fp32 rows; top-k reads the causal half of the fp32 scores and writes the
+    CSR."""
+    w = x.workload
+    tc = int(offs.num_chunks.sum())
+    qbar = torch.empty((hq * tc, 128), dtype=torch.float32, device=q.device)
+    kbar = torch.empty((hkv * tc, 128), dtype=torch.float32, device=q.device)
+    sc = torch.zeros(dhsa.scores_numel(offs, hq), dtype=torch.float32, device=q.device)
+    R, nnz = dhsa.csr_size(offs, hq, x.topk)
+    csr = dhsa.CSR(torch.empty(R + 1, dtype=torch.int32, device=q.device),
+                   torch.empty(max(nnz, 1), dtype=torch.int32, device=q.device), nnz)
+    fns = [lambda: dhsa.pool(q, offs, out=qbar), lambda: dhsa.pool(k, offs, out=kbar),
+           lambda: dhsa.chunk_scores(qbar, kbar, offs, hq, hkv, out=sc),
+           lambda: dhsa.topk_csr(sc, offs, hq, x.topk, out=csr)]
+    stream = torch.cuda.current_stream()
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    t = [statistics.mean(ts) for ts in timed_runs(torch, stream, fns, steps)]
+    L = w.batch * w.seq_len
+    bq = 2 * L * hq * 128 + 4 * hq * tc * 128
+    bk = 2 * L * hkv * 128 + 4 * hkv * tc * 128
+    causal = sum(hq * c * (c + 1) // 2 for c in offs.num_chunks.tolist())
+    btop = 4 * causal + 4 * (R + 1 + nnz)
+    res = {"steps": steps,
+           "pool_q_ms": t[0], "pool_q_GBps": bq / (t[0] * 1e-3) / 1e9,
+           "pool_k_ms": t[1], "pool_k_GBps": bk / (t[1] * 1e-3) / 1e9,
+           "pool_GBps": (bq + bk) / ((t[0] + t[1]) * 1e-3) / 1e9,
+           "pool_frac_of_hbm": (bq + bk) / ((t[0] + t[1]) * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+           "scores_ms": t[2],
+           "scores_GFLOP_per_s": 2 * 128 * causal / (t[2] * 1e-3) / 1e9,
+           "topk_ms": t[3], "topk_GBps": btop / (t[3] * 1e-3) / 1e9,
+           "topk_frac_of_hbm": btop / (t[3] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+           "how": "stage calls into preallocated buffers, HIP events around each; pooling "
+                  "counts the bf16 tensor read once and the fp32 pooled rows written; top-k "
+                  "counts the causal half of the fp32 scores read and the CSR written"}
+    log(f"[bench] mask stages: pool Q {t[0] * 1e3:.1f} us + K {t[1] * 1e3:.1f} us "
+        f"({res['pool_GBps']:.0f} GB/s), scores {t[2] * 1e3:.1f} us, top-k {t[3] * 1e3:.1f} us "
+        f"({res['topk_GBps']:.0f} GB/s)")
+    return res
 
 
 def time_variant(dhsa, synth, torch, x, offs, q, k, v, pf, hq, hkv, recent, steps, dev):
@@ -261,6 +424,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the widened-selection, NMS and batched-loop legs and the "
                          "reference ceilings (for profiling runs)")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the other layer shapes and the dense-causal 128K leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -326,6 +491,16 @@ def main():
     attn_avg = statistics.mean(attn_ms)
     mask_avg = statistics.mean(mask_ms)
     log(f"[bench] mask {mask_avg:.3f} ms  attention {attn_avg:.3f} ms  wall/step {ms_per_step:.3f} ms")
+    state = {}
+
+    def run_mask():
+        state["csr"] = mb(q, k)
+
+    def run_attn():
+        pf(q, k, v, state["csr"])
+
+    p_mask, p_attn = pages_protocol(torch, stream, [run_mask, run_attn])
+    log(f"[bench] median of 5 after 2 warmups: mask {p_mask:.3f} ms  attention {p_attn:.3f} ms")
 
     achieved = flops / (attn_avg * 1e-3) / 1e12
     traffic = None
@@ -336,6 +511,21 @@ def main():
                 traffic = pm.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None
+
+    stages = time_mask_stages(dhsa, torch, x, offs, q, k, hq, hkv, steps=args.steps)
+
+    layers = {}
+    if not args.no_layers:
+        for name in ("qwen25_3b_16k", "llama31_8b_32k"):
+            if name != w.name:
+                layers[name] = time_layer(dhsa, synth, torch, dev, name, steps=args.steps)
+        C = max(len(o) - 1 for o in x.offsets)
+        layers["dense_causal_" + w.name] = time_layer(
+            dhsa, synth, torch, dev, w.name, steps=3, topk=C, label="dense_causal_" + w.name, x=x)
+        d = layers["dense_causal_" + w.name]
+        d["sparse_speedup"] = d["ms_per_layer_median5"] / (p_mask + p_attn)
+        d["note"] = ("same layer and kernels with topk >= chunk count: every causal chunk kept; "
+                     "sparse_speedup = this median latency / the sparse layer's")
 
     variants = {}
     if not args.no_variants:
@@ -358,7 +548,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
-        cpu = cpu_baseline(x, None, hq, hkv)
+        cpu = cpu_baseline(x, hq, hkv)
 
     line = {
         "metric": "sparse prefill ms/layer + kept-tile TFLOP/s, Llama-3.1-8B layer shape @128K",
@@ -380,14 +570,19 @@ def main():
         "attention_ms": attn_avg,
         "mask_ms_median": statistics.median(mask_ms),
         "attention_ms_median": statistics.median(attn_ms),
+        "ms_per_layer_median5": p_mask + p_attn,
+        "mask_ms_median5": p_mask,
+        "attention_ms_median5": p_attn,
         "mask_GBps": mask_bytes / (mask_avg * 1e-3) / 1e9,
         "mask_hbm_frac": mask_bytes / (mask_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "mask_stages": stages,
         "kept_tile_TFLOP": flops / 1e12,
         "chunk_pairs": total_pairs,
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic},
         "ceilings": ceilings,
+        "layers": layers,
         "variants": variants,
         "cpu_baseline": cpu,
     }

@@ -210,7 +210,13 @@ int dhsa_build_mask_ex(const void* q, const void* k,
  * points.
  * The kernels bound-check CSR entries (entries outside [0, i] and row_ptr
  * values outside [0, nnz] are ignored), so a malformed CSR gives wrong
- * values but no out-of-bounds access. */
+ * values but no out-of-bounds access.
+ * Non-finite inputs: keys are processed in blocks of the row's gathered key
+ * stream; a block's padding past the stream's end loads the stream's first
+ * token, which every query row of the chunk sees.  A NaN or inf in K or V
+ * therefore reaches the rows that see it and, through the causal mask's
+ * exact-zero weights (0 * inf = NaN), the earlier query rows of its own
+ * diagonal chunk; no other row reads it. */
 int dhsa_sparse_prefill(const void* q, const void* k, const void* v,
                         int32_t batch, int32_t seq_len, int32_t num_q_heads,
                         int32_t num_kv_heads, int32_t head_dim,

@@ -1,6 +1,12 @@
-"""Builds libdhsa.so in-tree with hipcc for gfx950 (no CUDA, no other target).
+"""Builds libdhsa.so in-tree for gfx950 (no CUDA, no other target).
 
     python -m long_context_prefill_segmented_amd.build_lib
+
+Each source compiles in two passes, as hipcc's own single pass does
+internally: the device pass (gfx950 code object, bundled as a fat binary)
+and the host pass, which embeds that fat binary.  Splitting them lets the
+device-only flags (the packed-fp32 VALU forms switched off) reach the device
+compiler alone, so the host compiler never sees an unknown target feature.
 """
 from __future__ import annotations
 
@@ -18,15 +24,17 @@ LIB = os.path.join(PKG, "libdhsa.so")
 
 SOURCES = ["dhsa_api.hip", "pool.hip", "scores.hip", "topk.hip", "attn.hip", "nms.hip", "layer.hip"]
 
-HIPCC_FLAGS = [
+COMMON_FLAGS = [
+    "-x", "hip",
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    # packed fp32 VALU forms are kept out of the device code
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# device pass only: packed fp32 VALU forms are kept out of the device code
+DEVICE_FLAGS = ["--cuda-device-only", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+HOST_FLAGS = ["--cuda-host-only"]
 
 
 def hipcc() -> str:
@@ -36,26 +44,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def clang() -> str:
+    """The HIP compiler driver hipcc itself runs (clang++ -x hip)."""
+    for cand in (os.environ.get("HIP_CLANG"), "/opt/rocm/lib/llvm/bin/clang++"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("/opt/rocm/lib/llvm/bin/clang++ not found")
+
+
+def _run(cmd, what, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"{what} failed:\n{res.stdout}\n{res.stderr}")
+    return res
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libdhsa.so; returns the library path."""
-    cc = hipcc()
+    cc, hc = clang(), hipcc()
+    inc = ["-I", INCLUDE, "-I", CSRC]
     with tempfile.TemporaryDirectory(prefix="dhsa_build_") as tmp:
         objs = []
         for src in SOURCES:
+            path = os.path.join(CSRC, src)
+            fatbin = os.path.join(tmp, src.replace(".hip", ".fatbin"))
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
-                   os.path.join(CSRC, src), "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            res = subprocess.run(cmd, capture_output=True, text=True)
-            if res.returncode != 0:
-                raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+            _run([cc, *COMMON_FLAGS, *DEVICE_FLAGS, *inc, "-c", path, "-o", fatbin],
+                 f"device pass of {src}", verbose)
+            _run([cc, *COMMON_FLAGS, *HOST_FLAGS, *inc, "-Xclang", "-fcuda-include-gpubinary",
+                  "-Xclang", fatbin, "-c", path, "-o", obj], f"host pass of {src}", verbose)
             objs.append(obj)
         tmp_lib = os.path.join(tmp, "libdhsa.so")
-        cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+        _run([hc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib], "link",
+             verbose)
         os.replace(tmp_lib, LIB)
     return LIB
 

@@ -22,7 +22,7 @@
 //    into 64-key sub-tiles that may cross chunk boundaries, so short chunks
 //    waste no MFMA work on padding;
 //  * K and V sub-tiles go straight from global memory into LDS
-//    (global_load_lds, 16 bytes per lane, no staging registers), double
+//    (buffer_load_dwordx4 ... lds, 16 bytes per lane, no staging registers), double
 //    buffered: the loads of sub-tile j+1 are in flight while sub-tile j is
 //    computed, with one barrier per sub-tile.  Both tiles are row-major
 //    [64 keys][128 dims] with the 16-byte chunks of each row XOR-swizzled so
@@ -321,12 +321,24 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnParams p, SeqT
     const int Gd1 = s_diag[1];
     if (Gtot == 0) continue;
     const int nsub = (Gtot + kBN - 1) / kBN;
+    // stream positions past Gtot (the last sub-tile's padding) load the
+    // first token of the stream: it lies in the row's first non-empty kept
+    // chunk, an earlier chunk or the diagonal chunk's first token, so every
+    // query row of the tile sees it, and a non-finite value there reaches
+    // no row that could not see it anyway (the padding's weight is exactly
+    // 0, and 0 * inf would otherwise leak NaN into rows that never see the
+    // loaded key)
+    int tok_pad;
+    {
+      Cursor c0{-1, 0, 0, 0};
+      tok_pad = cursor_token(c0, 0, tbl_start, tbl_pref);
+    }
 
     Cursor cur{-1, 0, 0, 0};
     // direct-to-LDS loads of sub-tile js into (Kd, Vd)
     auto issue = [&](int js, uint16_t* Kd, uint16_t* Vd) {
       const int pos = js * kBN + kRowsPerWave * wv + lwalk;
-      const int tok = pos < Gtot ? cursor_token(cur, pos, tbl_start, tbl_pref) : 0;
+      const int tok = pos < Gtot ? cursor_token(cur, pos, tbl_start, tbl_pref) : tok_pad;
 #pragma unroll
       for (int u = 0; u < kLoadsPerMat; ++u) {
         const uint32_t tk = (uint32_t)__shfl(tok, 4 * u + lgrp, 64);

@@ -1,6 +1,5 @@
 // One 32x32 tile of chunk scores qbar . kbar^T on fp32 MFMA
-// (v_mfma_f32_32x32x2f32), shared by the stand-alone score kernel and the
-// fused score + top-k kernel so both produce bit-identical scores.
+// (v_mfma_f32_32x32x2f32), used by the chunk-score kernel.
 //
 // The contraction over the 128 dimensions is split by lane half: lanes 0-31
 // feed d in [0,64), lanes 32-63 feed d in [64,128); the chain order is

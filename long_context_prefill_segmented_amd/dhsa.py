@@ -203,13 +203,54 @@ def _workspace(nbytes: int, device):
     return torch.empty(max(nbytes, ALIGN), dtype=torch.uint8, device=device)
 
 
-def _check_qkv(q, k, v=None):
+def _check_tensor(name, t, shape, dtype, device):
+    """Raises ValueError unless t is a contiguous tensor of exactly this
+    shape and dtype on this device.  The shape is checked first, so a wrong
+    shape is reported whatever device the tensor is on."""
     torch = _torch()
-    for t in (q, k) + ((v,) if v is not None else ()):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda or t.dim() != 4:
-            raise ValueError("q/k/v must be contiguous CUDA bfloat16 [B, L, H, 128] tensors")
-    if k.shape[:2] != q.shape[:2] or (v is not None and v.shape != k.shape):
-        raise ValueError("q, k, v shapes disagree")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the offsets' device)")
+
+
+def _check_heads(hq: int, hkv: int):
+    if hq < 1 or hkv < 1 or hq % hkv != 0:
+        raise ValueError(f"num_q_heads {hq} must be a positive multiple of num_kv_heads {hkv}")
+
+
+def _check_qkv(offsets: "ChunkOffsets", hq: int, hkv: int, q, k, v=None):
+    """q [B, L, hq, 128], k and v [B, L, hkv, 128], bf16, contiguous, on the
+    offsets' device, B and L those of the offsets: the kernels take the
+    sequence length and every row count from the offsets, so a smaller
+    tensor would be read past its end."""
+    torch = _torch()
+    _check_heads(hq, hkv)
+    B, L = offsets.batch, offsets.seq_len
+    _check_tensor("q", q, (B, L, hq, HEAD_DIM), torch.bfloat16, offsets.device.device)
+    _check_tensor("k", k, (B, L, hkv, HEAD_DIM), torch.bfloat16, offsets.device.device)
+    if v is not None:
+        _check_tensor("v", v, (B, L, hkv, HEAD_DIM), torch.bfloat16, offsets.device.device)
+
+
+def _check_csr(offsets: "ChunkOffsets", hq: int, csr: "CSR"):
+    """row_ptr holds R + 1 entries (R = hq * sum_b C_b), col_idx at least
+    max(nnz, 1), both int32 on the offsets' device."""
+    torch = _torch()
+    R = hq * int(offsets.num_chunks.sum())
+    _check_tensor("csr.row_ptr", csr.row_ptr, (R + 1,), torch.int32, offsets.device.device)
+    if csr.nnz < 0:
+        raise ValueError(f"csr.nnz {csr.nnz} < 0")
+    ci = csr.col_idx
+    if not isinstance(ci, torch.Tensor) or ci.dim() != 1 or ci.numel() < max(csr.nnz, 1):
+        raise ValueError(f"csr.col_idx must be a 1-D tensor of at least {max(csr.nnz, 1)} entries")
+    _check_tensor("csr.col_idx", ci, (ci.numel(),), torch.int32, offsets.device.device)
 
 
 def scores_numel(offsets: ChunkOffsets, num_q_heads: int) -> int:
@@ -238,6 +279,7 @@ class MaskBuilder:
 
     def __call__(self, q, k, stream=None, row_budgets=None) -> CSR:
         o = self.offsets
+        _check_qkv(o, self.hq, self.hkv, q, k)
         scores = _dptr(self.scores) if self.scores is not None else None
         if row_budgets is None and self.recent == 0:
             check(lib.dhsa_build_mask(
@@ -258,9 +300,9 @@ class MaskBuilder:
 def build_mask(q, k, offsets: ChunkOffsets, topk: int, return_scores: bool = False,
                stream=None, row_budgets=None, recent: int = 0):
     """dhsa_build_mask(_ex): pooled chunk scores -> causal chunk selection as CSR."""
-    _check_qkv(q, k)
-    B, L, hq, _ = q.shape
-    hkv = k.shape[2]
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, L, H, 128] tensors")
+    hq, hkv = int(q.shape[2]), int(k.shape[2])
     mb = MaskBuilder(offsets, hq, hkv, topk, device=q.device, keep_scores=return_scores,
                      recent=recent)
     csr = mb(q, k, stream, row_budgets=row_budgets)
@@ -282,6 +324,8 @@ class Prefill:
 
     def __call__(self, q, k, v, csr: CSR, stream=None):
         o = self.offsets
+        _check_qkv(o, self.hq, self.hkv, q, k, v)
+        _check_csr(o, self.hq, csr)
         check(lib.dhsa_sparse_prefill(
             _dptr(q), _dptr(k), _dptr(v), o.batch, o.seq_len, self.hq, self.hkv, HEAD_DIM,
             _np_ptr(o.num_chunks), _np_ptr(o.host), _dptr(o.device), _dptr(csr.row_ptr),
@@ -294,44 +338,64 @@ class Prefill:
 def sparse_prefill(q, k, v, offsets: ChunkOffsets, csr: CSR, softmax_scale: float = 0.0,
                    return_lse: bool = False, stream=None):
     """dhsa_sparse_prefill: block-sparse causal attention over the kept tiles."""
-    _check_qkv(q, k, v)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k and v must be [B, L, H, 128] tensors")
     pf = Prefill(offsets, q.shape[2], k.shape[2], device=q.device, with_lse=return_lse,
                  softmax_scale=softmax_scale)
     return pf(q, k, v, csr, stream)
 
 
-def pool(x, offsets: ChunkOffsets, stream=None):
-    """dhsa_pool: fp32 [sum_b H*C_b, 128] pooled chunk representations."""
+def pool(x, offsets: ChunkOffsets, stream=None, out=None):
+    """dhsa_pool: fp32 [sum_b H*C_b, 128] pooled chunk representations
+    (written into `out` when given)."""
     torch = _torch()
-    _check_qkv(x, x)
-    B, L, H, _ = x.shape
-    out = torch.empty((H * int(offsets.num_chunks.sum()), HEAD_DIM), dtype=torch.float32,
-                      device=x.device)
+    if x.dim() != 4:
+        raise ValueError("x must be a [B, L, H, 128] tensor")
+    B, L, H = offsets.batch, offsets.seq_len, int(x.shape[2])
+    _check_tensor("x", x, (B, L, H, HEAD_DIM), torch.bfloat16, offsets.device.device)
+    shape = (H * int(offsets.num_chunks.sum()), HEAD_DIM)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check_tensor("out", out, shape, torch.float32, offsets.device.device)
     check(lib.dhsa_pool(_dptr(x), B, L, H, HEAD_DIM, _np_ptr(offsets.num_chunks),
                         _np_ptr(offsets.host), _dptr(offsets.device), _dptr(out),
                         _stream_ptr(stream)))
     return out
 
 
-def chunk_scores(qbar, kbar, offsets: ChunkOffsets, hq: int, hkv: int, stream=None):
-    """dhsa_chunk_scores: fp32 per sequence [Hq, C_b, C_b] (j > i untouched: NaN here)."""
+def chunk_scores(qbar, kbar, offsets: ChunkOffsets, hq: int, hkv: int, stream=None, out=None):
+    """dhsa_chunk_scores: fp32 per sequence [Hq, C_b, C_b] (j > i untouched: NaN
+    in a freshly allocated output; `out`, when given, keeps its values there)."""
     torch = _torch()
-    out = torch.full((scores_numel(offsets, hq),), float("nan"), dtype=torch.float32,
-                     device=qbar.device)
+    _check_heads(hq, hkv)
+    tc = int(offsets.num_chunks.sum())
+    _check_tensor("qbar", qbar, (hq * tc, HEAD_DIM), torch.float32, offsets.device.device)
+    _check_tensor("kbar", kbar, (hkv * tc, HEAD_DIM), torch.float32, offsets.device.device)
+    if out is None:
+        out = torch.full((scores_numel(offsets, hq),), float("nan"), dtype=torch.float32,
+                         device=qbar.device)
+    _check_tensor("out", out, (scores_numel(offsets, hq),), torch.float32,
+                  offsets.device.device)
     check(lib.dhsa_chunk_scores(_dptr(qbar), _dptr(kbar), offsets.batch, hq, hkv, HEAD_DIM,
                                 _np_ptr(offsets.num_chunks), _dptr(out), _stream_ptr(stream)))
     return out
 
 
 def topk_csr(scores, offsets: ChunkOffsets, hq: int, topk: int, stream=None,
-             row_budgets=None, recent: int = 0) -> CSR:
-    """dhsa_topk_csr(_ex): CSR from given fp32 chunk scores."""
+             row_budgets=None, recent: int = 0, out: Optional[CSR] = None) -> CSR:
+    """dhsa_topk_csr(_ex): CSR from given fp32 chunk scores (into `out`, a CSR
+    of dhsa_csr_capacity's sizes, when given)."""
     torch = _torch()
-    if scores.dtype != torch.float32 or not scores.is_contiguous():
-        raise ValueError("scores must be contiguous float32")
+    _check_tensor("scores", scores, (scores_numel(offsets, hq),), torch.float32,
+                  offsets.device.device)
     R, nnz = csr_capacity(offsets, hq, topk, recent)
-    csr = CSR(torch.empty(R + 1, dtype=torch.int32, device=scores.device),
-              torch.empty(max(nnz, 1), dtype=torch.int32, device=scores.device), nnz)
+    if out is None:
+        out = CSR(torch.empty(R + 1, dtype=torch.int32, device=scores.device),
+                  torch.empty(max(nnz, 1), dtype=torch.int32, device=scores.device), nnz)
+    _check_csr(offsets, hq, out)
+    if out.col_idx.numel() < max(nnz, 1):
+        raise ValueError(f"out.col_idx holds {out.col_idx.numel()} entries, {nnz} needed")
+    csr = out
     if row_budgets is None and recent == 0:
         check(lib.dhsa_topk_csr(_dptr(scores), offsets.batch, hq, _np_ptr(offsets.num_chunks),
                                 topk, _dptr(csr.row_ptr), _dptr(csr.col_idx),
@@ -374,8 +438,8 @@ class Layer:
         self.num_groups = 0
 
     def __call__(self, q, k, v, row_budgets=None, stream=None):
-        _check_qkv(q, k, v)
         o = self.offsets
+        _check_qkv(o, self.hq, self.hkv, q, k, v)
         R = self.hq * int(o.num_chunks.sum())
         ng = _i32()
         check(lib.dhsa_layer_forward(

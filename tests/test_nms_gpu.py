@@ -119,10 +119,35 @@ def test_nms_full_size_feeds_the_path(name):
         want = orc.nms_boundaries(p[b].astype(np.float64), g, 0.5)
         np.testing.assert_array_equal(co.host[starts[b]:starts[b + 1]], want)
         say(f"  {name} b{b}: {len(want) - 1} chunks from NMS, {len(x.offsets[b]) - 1} drawn")
-    # the NMS offsets drive the mask and the attention without error
+    # the NMS offsets drive the mask and the attention: the selection equals
+    # the oracle's on the GPU's own fp32 scores, and sampled attention rows
+    # (first, last, longest chunk and seeded picks) equal the oracle's
+    assert int(co.num_chunks.max()) <= 2048
     q, k, v = (dhsa.bf16_from_bits(a) for a in (x.q, x.k, x.v))
-    if int(co.num_chunks.max()) <= 2048:
-        csr = dhsa.build_mask(q, k, co, x.topk)
-        out = dhsa.sparse_prefill(q, k, v, co, csr)
-        torch.cuda.synchronize()
-        assert torch.isfinite(out.float()).all()
+    hq, G = w.num_q_heads, w.num_q_heads // w.num_kv_heads
+    csr, flat = dhsa.build_mask(q, k, co, x.topk, return_scores=True)
+    out = dhsa.sparse_prefill(q, k, v, co, csr)
+    torch.cuda.synchronize()
+    rows = orc.csr_to_rows(csr.row_ptr.cpu().numpy(), csr.col_idx.cpu().numpy()[:csr.nnz],
+                           co.num_chunks, hq)
+    scores = flat.cpu().numpy()
+    got_all = orc.widen_bf16(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    rng = np.random.default_rng(11)
+    spos = 0
+    for b in range(w.batch):
+        o = co.host[starts[b]:starts[b + 1]].astype(np.int64)
+        C = len(o) - 1
+        gs = scores[spos:spos + hq * C * C].reshape(hq, C, C).astype(np.float64)
+        spos += hq * C * C
+        assert orc.select_topk(gs, x.topk) == rows[b]
+        qf, kf, vf = (orc.widen_bf16(a[b]) for a in (x.q, x.k, x.v))
+        n = np.diff(o)
+        picks = {(0, 0), (hq - 1, C - 1), (hq // 2, int(np.argmax(n)))}
+        picks |= {(int(rng.integers(0, hq)), int(rng.integers(0, C))) for _ in range(8)}
+        for (h, i) in sorted(picks):
+            ref, _ = orc.chunk_attention(qf, kf, vf, o, rows[b][h][i], i, h, h // G,
+                                         1.0 / np.sqrt(128))
+            got = got_all[b, o[i]:o[i + 1], h]
+            err = np.abs(got - ref)
+            assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), (name, b, h, i, float(err.max()))
+        say(f"  {name} b{b}: selection bit-exact, {len(picks)} attention rows within the bar")

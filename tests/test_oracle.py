@@ -464,3 +464,22 @@ def test_nms_closed_forms():
     # NaN never becomes a boundary
     p[57] = np.nan
     assert orc.nms_boundaries(p, 16, 0.5).tolist() == [0, 20, 90, 150, 200]
+
+
+def test_widen_bf16_matches_torch_on_every_bit_pattern():
+    """bf16 -> float64 widening is exact: every one of the 65,536 bit
+    patterns (signed zeros, subnormals, the largest finite values, infinities
+    and NaNs) widens to the value torch's own bfloat16 -> float64 conversion
+    gives."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = orc.widen_bf16(bits)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # the sign of zero survives
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0x0000])
+    assert got[0x7F80] == np.inf and got[0xFF80] == -np.inf
+    # smallest subnormal: 2^-133
+    assert got[0x0001] == 2.0 ** -133

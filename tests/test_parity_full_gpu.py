@@ -74,6 +74,8 @@ def test_full_size_layer(name):
             bound = 1e-5 * qn[h][:, None] * kn[h // G][None, :]
             err = np.abs(gs[h] - s64[h])
             assert np.all(err[low] <= bound[low]), (name, b, h, float(err[low].max()))
+        # the fixed rule on the GPU's own fp32 scores: bit-exact
+        assert orc.select_topk(gs.astype(np.float64), x.topk) == gpu_rows[b], (name, b)
         # mask: equal, or a near-tie within the score bound
         near = 0
         for h in range(hq):
@@ -122,11 +124,17 @@ def test_full_size_layer(name):
         kf = orc.widen_bf16(x.k[b])
         vf = orc.widen_bf16(x.v[b])
         rows = ref_rows_all[b]
-        for (h, i) in [(0, C // 3), (hq - 1, (2 * C) // 3), (1 % hq, C - 1)]:
-            ref, _ = orc.chunk_attention(qf, kf, vf, o, rows[h][i], i, h, h // G,
-                                         1.0 / np.sqrt(128))
-            got = orc.widen_bf16(out2_np[b, o[i]:o[i + 1], h])
-            assert np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref)), (name, b, h, i)
+        # every query chunk of two heads (the first and the last; the last
+        # head's KV group differs from the first's)
+        for h in sorted({0, hq - 1}):
+            for i in range(C):
+                ref, _ = orc.chunk_attention(qf, kf, vf, o, rows[h][i], i, h, h // G,
+                                             1.0 / np.sqrt(128))
+                got = orc.widen_bf16(out2_np[b, o[i]:o[i + 1], h])
+                err = np.abs(got - ref)
+                assert np.all(err <= ATOL + RTOL * np.abs(ref)), (name, b, h, i, float(err.max()))
+        say(f"[full] {name}: sequence {b}: all {C} query chunks of heads 0 and {hq - 1} "
+            f"on the oracle mask within the bar")
         del qf, kf, vf
     say(f"[full] {name}: ok")
 

@@ -404,3 +404,37 @@ def test_tile_heights_agree_to_rounding(name, monkeypatch):
     exact = np.mean(o1 == o2)
     say(f"  {name}: {exact:.1%} of outputs bitwise equal")
     assert exact > 0.95
+
+
+@pytest.mark.parametrize("name", ["mid_ragged", "batch5"])
+def test_nonfinite_values_reach_only_rows_that_see_them(name, block_m):
+    """Non-finite values planted in token 0 (V NaN in the first sequence, V
+    +inf and K NaN in the others) must not leak into rows that do not keep
+    chunk 0: the padding of a row's last key block loads a key of the row's
+    own stream, never token 0.  Rows that keep chunk 0 see the value and are
+    not compared; every other row must equal the oracle on the same inputs."""
+    c = get_case(name)
+    qb, kb, vb = (a.copy() for a in (c.x.q, c.x.k, c.x.v))
+    vb[0, 0] = 0x7FC0                      # NaN
+    vb[1:, 0] = 0x7F80                     # +inf
+    kb[1:, 0] = 0x7FC0
+    q, k, v = (dhsa.bf16_from_bits(a) for a in (qb, kb, vb))
+    out = dhsa.sparse_prefill(q, k, v, c.offs, dhsa.csr_from_host(c.rp, c.ci))
+    torch.cuda.synchronize()
+    got = orc.widen_bf16(to_np_bf16(out))
+    G = c.hq // c.hkv
+    checked = 0
+    for b in range(c.B):
+        o = c.x.offsets[b]
+        kf, vf = orc.widen_bf16(kb[b]), orc.widen_bf16(vb[b])
+        for h in range(c.hq):
+            for i in range(len(o) - 1):
+                row = c.ref[b]["rows"][h][i]
+                if 0 in row:
+                    continue
+                ref, _ = orc.chunk_attention(c.ref[b]["q"], kf, vf, o, row, i, h, h // G,
+                                             1.0 / math.sqrt(128))
+                assert_attention_close(got[b, o[i]:o[i + 1], h], ref, f"{name} b{b} h{h} i{i}")
+                checked += 1
+    say(f"  {name}: {checked} rows without chunk 0 finite and within the bar")
+    assert checked > 0
