@@ -16,7 +16,8 @@
  * top-k) for stage-wise checking.  dhsa_build_mask_ex and dhsa_topk_csr_ex
  * widen the selection rule with per-row budgets and a recent-chunk window.
  * dhsa_nms_boundaries, the step before the path, turns per-token boundary
- * scores into chunk offsets.
+ * scores into chunk offsets.  dhsa_sparse_prefill_noalloc is
+ * dhsa_sparse_prefill for callers that cannot allocate a workspace.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -40,7 +41,8 @@
  *
  * Ownership.  The caller allocates and frees every buffer (inputs, outputs,
  * workspaces).  The library allocates nothing and keeps no state besides a
- * thread-local error string.
+ * thread-local error string, and, for dhsa_sparse_prefill_noalloc only, one
+ * static 1 MiB device array per GPU and its per-device address.
  *
  * Asynchrony.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  * stream) and the calls never synchronise.  Host-side inputs may be released
@@ -70,6 +72,7 @@ extern "C" {
 #define DHSA_MAX_BATCH 64
 #define DHSA_MAX_CHUNKS 2048
 #define DHSA_NMS_MAX_LEN 524288
+#define DHSA_NOALLOC_MAX_TILES 65536
 
 typedef enum dhsa_status {
   DHSA_OK = 0,
@@ -225,6 +228,28 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v,
                         const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                         float softmax_scale, void* out, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* dhsa_sparse_prefill without a workspace argument, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  The query-tile
+ * list lives in a static device array of the library (DHSA_NOALLOC_MAX_TILES
+ * int4 entries, 1 MiB, one copy per GPU, held until the process ends); the
+ * call allocates nothing.  Arguments, outputs and results are those of
+ * dhsa_sparse_prefill (bit-identical: the same kernels run on the same
+ * tiles).  Errors: those of dhsa_sparse_prefill, and DHSA_ERR_CAPACITY
+ * when the problem needs more query tiles than the array holds (a tile is
+ * at most 128 query rows of one chunk, so sum_b sum_c ceil(n_c / 128) <=
+ * DHSA_NOALLOC_MAX_TILES always fits); the first call on a device looks up
+ * the array's address (DHSA_ERR_HIP if that fails).  Every call on one GPU
+ * shares its array: calls that overlap in time on one GPU (two streams, or
+ * two host threads) race on it and give undefined results; serialise them. */
+int dhsa_sparse_prefill_noalloc(const void* q, const void* k, const void* v,
+                                int32_t batch, int32_t seq_len, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                const int32_t* num_chunks, const int32_t* chunk_offsets,
+                                const int32_t* chunk_offsets_dev,
+                                const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                float softmax_scale, void* out, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------
  * Stage calls (the steps of dhsa_build_mask one at a time)

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "dhsa_internal.h"
 
@@ -215,7 +216,7 @@ const char* dhsa_status_string(int status) {
 
 const char* dhsa_last_error(void) { return dhsa::g_err; }
 
-int dhsa_version(void) { return 101; }
+int dhsa_version(void) { return 102; }
 
 int dhsa_csr_capacity(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
                       int32_t topk, int32_t recent, int32_t* num_rows, int64_t* nnz) {
@@ -458,13 +459,57 @@ int dhsa_build_mask(const void* q, const void* k, int32_t batch, int32_t seq_len
                             workspace_bytes, stream);
 }
 
-int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t batch,
+}  // extern "C"
+
+namespace dhsa {
+namespace {
+
+// The query-tile list of dhsa_sparse_prefill_noalloc lives here instead of a
+// caller workspace.  Each GPU holds its own copy; its device address comes
+// from hipGetSymbolAddress on the first call on that device.
+__device__ __attribute__((aligned(256))) int4 scratch[DHSA_NOALLOC_MAX_TILES];
+constexpr size_t kScratchBytes = sizeof(int4) * DHSA_NOALLOC_MAX_TILES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per
+// device, with that device current); nullptr and a message on failure.
+void* scratch_address(int* status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(DHSA_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                   kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *status = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// dhsa_sparse_prefill; with use_scratch the tile list goes to this device's
+// static scratch array (workspace and workspace_bytes are ignored).
+int sparse_prefill_impl(const void* q, const void* k, const void* v, int32_t batch,
                         int32_t seq_len, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, const int32_t* num_chunks, const int32_t* chunk_offsets,
                         const int32_t* chunk_offsets_dev, const int32_t* row_ptr,
                         const int32_t* col_idx, int64_t nnz, float softmax_scale, void* out,
-                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !chunk_offsets_dev || !row_ptr || !out || !workspace)
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                        bool use_scratch) {
+  if (!q || !k || !v || !chunk_offsets_dev || !row_ptr || !out || (!use_scratch && !workspace))
     return fail(DHSA_ERR_NULL_POINTER, "NULL device pointer");
   if (nnz > 0 && !col_idx) return fail(DHSA_ERR_NULL_POINTER, "col_idx is NULL");
   if (nnz < 0 || nnz > INT32_MAX) return fail(DHSA_ERR_CSR, "nnz %lld out of range", (long long)nnz);
@@ -490,6 +535,16 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
     return fail(DHSA_ERR_UNSUPPORTED, "too many query tiles");
   // the workspace bound (tiles of the smaller height) also covers the two lists
   const size_t need = align_up((size_t)(ntiles + nnarrow) * sizeof(int4));
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(DHSA_ERR_CAPACITY,
+                  "%lld query tiles exceed the static scratch of %d tiles (DHSA_NOALLOC_MAX_TILES)",
+                  (long long)(ntiles + nnarrow), DHSA_NOALLOC_MAX_TILES);
+    int st_fail = DHSA_OK;
+    workspace = scratch_address(&st_fail);
+    if (workspace == nullptr) return st_fail;
+    workspace_bytes = kScratchBytes;
+  }
   if (workspace_bytes < need)
     return fail(DHSA_ERR_CAPACITY, "workspace %zu < %zu bytes", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
@@ -530,6 +585,34 @@ int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t bat
   e = launch_attention(p, st, strm);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
+}
+
+}  // namespace
+}  // namespace dhsa
+
+extern "C" {
+
+int dhsa_sparse_prefill(const void* q, const void* k, const void* v, int32_t batch,
+                        int32_t seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, const int32_t* num_chunks, const int32_t* chunk_offsets,
+                        const int32_t* chunk_offsets_dev, const int32_t* row_ptr,
+                        const int32_t* col_idx, int64_t nnz, float softmax_scale, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return dhsa::sparse_prefill_impl(q, k, v, batch, seq_len, num_q_heads, num_kv_heads, head_dim,
+                                   num_chunks, chunk_offsets, chunk_offsets_dev, row_ptr, col_idx,
+                                   nnz, softmax_scale, out, lse, workspace, workspace_bytes, stream,
+                                   false);
+}
+
+int dhsa_sparse_prefill_noalloc(const void* q, const void* k, const void* v, int32_t batch,
+                                int32_t seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, const int32_t* num_chunks,
+                                const int32_t* chunk_offsets, const int32_t* chunk_offsets_dev,
+                                const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                float softmax_scale, void* out, float* lse, void* stream) {
+  return dhsa::sparse_prefill_impl(q, k, v, batch, seq_len, num_q_heads, num_kv_heads, head_dim,
+                                   num_chunks, chunk_offsets, chunk_offsets_dev, row_ptr, col_idx,
+                                   nnz, softmax_scale, out, lse, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

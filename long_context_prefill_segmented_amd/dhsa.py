@@ -34,6 +34,7 @@ HEAD_DIM = 128
 MAX_BATCH = 64
 MAX_CHUNKS = 2048
 NMS_MAX_LEN = 524288
+NOALLOC_MAX_TILES = 65536
 
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -62,6 +63,9 @@ _SIGNATURES = {
     "dhsa_sparse_prefill": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                            _vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp, _vp, _sz,
                                            _vp]),
+    "dhsa_sparse_prefill_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                   _vp, _vp, _vp, _vp, _vp, _i64, _f32, _vp, _vp,
+                                                   _vp]),
     "dhsa_pool": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "dhsa_chunk_scores": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "dhsa_topk_csr": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _i64, _vp]),
@@ -343,6 +347,27 @@ def sparse_prefill(q, k, v, offsets: ChunkOffsets, csr: CSR, softmax_scale: floa
     pf = Prefill(offsets, q.shape[2], k.shape[2], device=q.device, with_lse=return_lse,
                  softmax_scale=softmax_scale)
     return pf(q, k, v, csr, stream)
+
+
+def sparse_prefill_noalloc(q, k, v, offsets: ChunkOffsets, csr: CSR, out, lse=None,
+                           softmax_scale: float = 0.0, stream=None):
+    """dhsa_sparse_prefill_noalloc into caller-provided out (bf16 [B, L, Hq,
+    128]) and optional lse (fp32 [B, Hq, L]): the library's static tile
+    array replaces the workspace, so the call allocates nothing."""
+    torch = _torch()
+    hq, hkv = int(q.shape[2]), int(k.shape[2])
+    _check_qkv(offsets, hq, hkv, q, k, v)
+    _check_csr(offsets, hq, csr)
+    B, L = offsets.batch, offsets.seq_len
+    _check_tensor("out", out, (B, L, hq, HEAD_DIM), torch.bfloat16, offsets.device.device)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, hq, L), torch.float32, offsets.device.device)
+    check(lib.dhsa_sparse_prefill_noalloc(
+        _dptr(q), _dptr(k), _dptr(v), B, L, hq, hkv, HEAD_DIM, _np_ptr(offsets.num_chunks),
+        _np_ptr(offsets.host), _dptr(offsets.device), _dptr(csr.row_ptr), _dptr(csr.col_idx),
+        csr.nnz, float(softmax_scale), _dptr(out), _dptr(lse) if lse is not None else None,
+        _stream_ptr(stream)))
+    return out
 
 
 def pool(x, offsets: ChunkOffsets, stream=None, out=None):

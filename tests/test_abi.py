@@ -43,7 +43,7 @@ def test_every_declared_function_is_exported():
 def test_binding_limits_match_the_header():
     text = open(HEADER).read()
     defs = dict(re.findall(r"^#define DHSA_(\w+) (\d+)", text, re.M))
-    for name in ("HEAD_DIM", "MAX_BATCH", "MAX_CHUNKS", "NMS_MAX_LEN"):
+    for name in ("HEAD_DIM", "MAX_BATCH", "MAX_CHUNKS", "NMS_MAX_LEN", "NOALLOC_MAX_TILES"):
         assert int(defs[name]) == getattr(dhsa, name), name
 
 
@@ -193,6 +193,37 @@ def test_sparse_prefill_rejects_bad_arguments():
     assert _prefill(seq_len=L, hq=16, hkv=16, nc=[1], offs=[0, L]) == EUNSUP
     assert b"4 GiB" in lib.dhsa_last_error()
     assert _prefill(seq_len=L, hq=16, hkv=8, nc=[1], offs=[0, L], ws_bytes=8) == ECAP
+
+
+def _prefill_noalloc(**kw):
+    a = dict(batch=1, seq_len=100, hq=4, hkv=2, hd=128, nc=[3], offs=[0, 10, 50, 100],
+             row_ptr=FAKE, col_idx=FAKE, nnz=20, scale=0.0, out=FAKE, lse=None)
+    a.update(kw)
+    nc = _arr(a["nc"])
+    offs = _arr(a["offs"])
+    return lib.dhsa_sparse_prefill_noalloc(FAKE, FAKE, FAKE, a["batch"], a["seq_len"], a["hq"],
+                                           a["hkv"], a["hd"], nc.ctypes.data, offs.ctypes.data,
+                                           FAKE, a["row_ptr"], a["col_idx"], a["nnz"], a["scale"],
+                                           a["out"], a["lse"], None)
+
+
+@cpu_only
+def test_sparse_prefill_noalloc_rejects_bad_arguments():
+    """The no-alloc variant checks everything dhsa_sparse_prefill checks, and
+    rejects a problem whose query tiles exceed its static array, all on the
+    host before any device access."""
+    assert _prefill_noalloc(out=None) == ENULL
+    assert _prefill_noalloc(row_ptr=None) == ENULL
+    assert _prefill_noalloc(nnz=-1) == ECSR
+    assert _prefill_noalloc(hd=64) == ESHAPE
+    assert _prefill_noalloc(offs=[0, 10, 50, 99]) == EOFF
+    assert _prefill_noalloc(scale=float("nan")) == ESHAPE
+    # 64 sequences of 2048 one-token chunks: 131,072 one-row tiles > 65,536
+    B, L = 64, 2048
+    nc = [L] * B
+    offs = list(range(L + 1)) * B
+    assert _prefill_noalloc(batch=B, seq_len=L, hq=1, hkv=1, nc=nc, offs=offs, nnz=1) == ECAP
+    assert b"static scratch" in lib.dhsa_last_error()
 
 
 @cpu_only
