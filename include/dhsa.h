@@ -114,8 +114,10 @@ int dhsa_csr_size(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
 int dhsa_csr_capacity(int32_t batch, const int32_t* num_chunks, int32_t num_q_heads,
                       int32_t topk, int32_t recent, int32_t* num_rows, int64_t* nnz);
 
-/* Bytes of device workspace dhsa_build_mask needs: pooled Q and K (fp32) and
- * the chunk-score matrices (fp32), each 256-byte aligned. */
+/* Bytes of device workspace dhsa_build_mask needs: pooled Q and K (fp32),
+ * the chunk-score matrices (fp32) and the pooling order (one int32 per
+ * chunk: the pooling grid runs the chunks longest first), each 256-byte
+ * aligned. */
 int dhsa_mask_workspace_size(int32_t batch, const int32_t* num_chunks,
                              int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, size_t* bytes);

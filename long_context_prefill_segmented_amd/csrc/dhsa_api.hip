@@ -255,6 +255,7 @@ int dhsa_mask_workspace_size(int32_t batch, const int32_t* num_chunks, int32_t n
   size_t n = align_up((size_t)num_q_heads * tc * kHeadDim * sizeof(float));
   n += align_up((size_t)num_kv_heads * tc * kHeadDim * sizeof(float));
   n += align_up((size_t)score_elems(batch, num_chunks, num_q_heads) * sizeof(float));
+  n += align_up((size_t)tc * sizeof(int32_t));  // pooling order, longest chunk first
   *bytes = n;
   return ok();
 }
@@ -331,7 +332,7 @@ int dhsa_pool(const void* x, int32_t batch, int32_t seq_len, int32_t num_heads, 
   fill_table(st, batch, num_chunks, num_heads, 0);
   hipError_t e = launch_pool(static_cast<const uint16_t*>(x), pooled, num_heads, nullptr, nullptr, 0,
                              (int32_t)total_chunks(batch, num_chunks), chunk_offsets_dev, st, seq_len,
-                             static_cast<hipStream_t>(stream));
+                             nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   return ok();
 }
@@ -428,6 +429,8 @@ int dhsa_build_mask_ex(const void* q, const void* k, int32_t batch, int32_t seq_
   float* kbar = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)num_kv_heads * tc * kHeadDim * sizeof(float));
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)score_elems(batch, num_chunks, num_q_heads) * sizeof(float));
+  int32_t* order = reinterpret_cast<int32_t*>(ws);
 
   const int32_t k_dev = topk < cmax ? topk : cmax;
   const int32_t w_dev = recent < cmax ? recent : cmax;
@@ -436,7 +439,7 @@ int dhsa_build_mask_ex(const void* q, const void* k, int32_t batch, int32_t seq_
   hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e = launch_pool(static_cast<const uint16_t*>(q), qbar, num_q_heads,
                              static_cast<const uint16_t*>(k), kbar, num_kv_heads, (int32_t)tc,
-                             chunk_offsets_dev, st, seq_len, strm);
+                             chunk_offsets_dev, st, seq_len, order, strm);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   e = launch_scores(qbar, kbar, scores, num_q_heads, num_kv_heads, st,
                     score_tiles(batch, num_chunks, num_q_heads), strm);

@@ -43,10 +43,15 @@ __device__ __forceinline__ int find_seq(const T* starts, int batch, T x) {
 }
 
 // kernels' launchers (each returns hipGetLastError() of its launch)
+// order (nullable, total_chunks int32 of device scratch): the pooling grid
+// then runs the chunks longest first (a one-workgroup sort fills it), used
+// up to kPoolOrderMaxChunks chunks in all
+constexpr int kPoolOrderMaxChunks = 16384;
 hipError_t launch_pool(const uint16_t* x0, float* out0, int32_t h0,
                        const uint16_t* x1, float* out1, int32_t h1,
                        int32_t total_chunks, const int32_t* offs_dev,
-                       const SeqTable& st, int32_t seq_len, hipStream_t stream);
+                       const SeqTable& st, int32_t seq_len, int32_t* order,
+                       hipStream_t stream);
 
 hipError_t launch_scores(const float* qbar, const float* kbar, float* scores,
                          int32_t hq, int32_t hkv, const SeqTable& st,

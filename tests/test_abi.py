@@ -117,7 +117,8 @@ def test_workspace_sizes():
     assert lib.dhsa_mask_workspace_size(2, nc.ctypes.data, 4, 2, 128, ctypes.byref(n)) == OK
     def al(x):
         return (x + 255) // 256 * 256
-    assert n.value == al(4 * 8 * 128 * 4) + al(2 * 8 * 128 * 4) + al(4 * (9 + 25) * 4)
+    # pooled Q, pooled K, the score matrices, the pooling order (one int32 per chunk)
+    assert n.value == al(4 * 8 * 128 * 4) + al(2 * 8 * 128 * 4) + al(4 * (9 + 25) * 4) + al(4 * 8)
     assert lib.dhsa_mask_workspace_size(2, nc.ctypes.data, 4, 3, 128, ctypes.byref(n)) == ESHAPE
     assert lib.dhsa_mask_workspace_size(2, nc.ctypes.data, 4, 2, 64, ctypes.byref(n)) == ESHAPE
     offs = _arr([0, 100, 300, 301, 0, 1, 2, 129, 256, 301])
@@ -332,15 +333,15 @@ def test_layer_workspace_size_parts():
     offs = [0, 10, 50, 100, 0, 60, 100]
 
     def single(c, offsets):
-        # mask (pooled Q, K, scores) + row_ptr + col_idx + query tiles
-        mask = al(4 * c * 128 * 4) + al(2 * c * 128 * 4) + al(4 * c * c * 4)
+        # mask (pooled Q, K, scores, pooling order) + row_ptr + col_idx + query tiles
+        mask = al(4 * c * 128 * 4) + al(2 * c * 128 * 4) + al(4 * c * c * 4) + al(4 * c)
         nnz = 4 * sum(min(2, i + 1) for i in range(c))
         tiles = sum((offsets[i + 1] - offsets[i] + 127) // 128 for i in range(c))
         return al(mask) + al(4 * (4 * c + 1)) + al(4 * nnz) + al(16 * tiles)
     s, n1 = _layer_ws(nc, offs, group=1)
     assert s == OK and n1 == max(single(3, offs[:4]), single(2, offs[4:]))
     s, n2 = _layer_ws(nc, offs, group=2)
-    mask = al(4 * 5 * 128 * 4) + al(2 * 5 * 128 * 4) + al(4 * (9 + 4) * 4)
+    mask = al(4 * 5 * 128 * 4) + al(2 * 5 * 128 * 4) + al(4 * (9 + 4) * 4) + al(4 * 5)
     nnz = 4 * (5 + 3)
     assert s == OK and n2 == al(mask) + al(4 * 21) + al(4 * nnz) + al(16 * 5)
     assert _layer_ws(nc, offs, group=0)[0] == ESHAPE

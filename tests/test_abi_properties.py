@@ -84,7 +84,8 @@ def test_mask_workspace(lens, heads):
     assert lib.dhsa_mask_workspace_size(nc.size, nc.ctypes.data, hq, hkv, 128,
                                         ctypes.byref(n)) == OK
     tc = int(nc.sum())
-    want = align(hq * tc * 512) + align(hkv * tc * 512) + align(4 * hq * int((nc.astype(np.int64) ** 2).sum()))
+    want = (align(hq * tc * 512) + align(hkv * tc * 512)
+            + align(4 * hq * int((nc.astype(np.int64) ** 2).sum())) + align(4 * tc))
     assert n.value == want
     assert lib.dhsa_mask_workspace_size(nc.size, nc.ctypes.data, hq, hkv, 64,
                                         ctypes.byref(n)) == ESHAPE
