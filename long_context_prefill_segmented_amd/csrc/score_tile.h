@@ -15,12 +15,6 @@ namespace dhsa {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ void load_half_row(const float* p, bool ok, float4* v) {
-#pragma unroll
-  for (int u = 0; u < 16; ++u)
-    v[u] = ok ? reinterpret_cast<const float4*>(p)[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
 __device__ __forceinline__ f32x16_t score_tile(const float4* qv, const float4* kv) {
   f32x16_t acc;
 #pragma unroll

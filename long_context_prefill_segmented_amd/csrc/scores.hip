@@ -6,7 +6,13 @@
 // (v_mfma_f32_32x32x2f32), accumulating over the 128 dimensions in a fixed
 // order, so scores are reproducible run to run.  The contraction index is
 // split by lane half: lanes 0-31 feed d in [0,64), lanes 32-63 feed d in
-// [64,128), so each lane streams one contiguous 256-byte half row.
+// [64,128).
+//
+// In that operand layout each lane owns one row, so loading it straight from
+// memory makes every 64-lane load touch 64 cache lines.  The 32 query rows
+// and then the 32 key rows are instead read row-contiguously (each load
+// instruction covers two whole 512-byte rows) into an LDS block padded by 16
+// bytes per row, and each lane takes its half row from there.
 #include "score_tile.h"
 
 namespace dhsa {
@@ -15,6 +21,31 @@ namespace {
 struct ScoreGrid {
   int32_t stbase[kMaxBatch + 1];  // first tile of each sequence
 };
+
+constexpr int kStageStride = kHeadDim / 4 + 1;  // float4 per staged row (one of padding)
+
+// Rows r0 .. r0+31 of a [*, 128] fp32 matrix (rows >= nrows read as zero)
+// into this lane's operand half row v[0..15] (row lane & 31, floats
+// 64 * (lane >> 5) ..): load u of a lane reads row 2u + lane/32, floats
+// 4 * (lane & 31) .., so each load instruction covers two whole rows; the
+// rows then pass through the LDS block stage.
+__device__ __forceinline__ void load_block(const float* base, int r0, int nrows, int lane,
+                                           float4* stage, float4* v) {
+  const float4* src = reinterpret_cast<const float4*>(base);
+  float4 t[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int r = 2 * u + (lane >> 5);
+    t[u] = r0 + r < nrows ? src[(size_t)(r0 + r) * (kHeadDim / 4) + (lane & 31)]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();  // the previous block's reads are done
+#pragma unroll
+  for (int u = 0; u < 16; ++u) stage[(2 * u + (lane >> 5)) * kStageStride + (lane & 31)] = t[u];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 16; ++u) v[u] = stage[(lane & 31) * kStageStride + 16 * (lane >> 5) + u];
+}
 
 __global__ __launch_bounds__(64) void scores_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kbar,
@@ -38,14 +69,15 @@ __global__ __launch_bounds__(64) void scores_kernel(const float* __restrict__ qb
   const int lane = threadIdx.x;
   const int row = lane & 31;
   const int half = lane >> 5;
-  const bool qok = i0 + row < C;
-  const bool kok = j0 + row < C;
-  const float* qp = qbar + ((size_t)hq * st.cbase[b] + (size_t)h * C + (i0 + row)) * kHeadDim + 64 * half;
-  const float* kp = kbar + ((size_t)hkv * st.cbase[b] + (size_t)(h / G) * C + (j0 + row)) * kHeadDim + 64 * half;
+  const float* qp = qbar + ((size_t)hq * st.cbase[b] + (size_t)h * C) * kHeadDim;
+  const float* kp = kbar + ((size_t)hkv * st.cbase[b] + (size_t)(h / G) * C) * kHeadDim;
 
+  // (issuing the key rows' loads before staging the query rows measured no
+  // faster and holds 64 more registers)
+  __shared__ float4 stage[32 * kStageStride];
   float4 qv[16], kv[16];
-  load_half_row(qp, qok, qv);
-  load_half_row(kp, kok, kv);
+  load_block(qp, i0, C, lane, stage, qv);
+  load_block(kp, j0, C, lane, stage, kv);
   const f32x16_t acc = score_tile(qv, kv);
   // accumulator layout: lane -> column j0 + (lane & 31); register r -> row
   // i0 + 8*(r/4) + 4*(lane/32) + r%4

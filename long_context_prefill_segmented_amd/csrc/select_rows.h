@@ -13,12 +13,16 @@
 // ranks below every number.
 //
 // One wavefront owns one row.  Candidate j sits in lane j % 64, slot j / 64,
-// as an order-preserving 32-bit key of its score.  Each of the k-1 rounds
-// takes every lane's best untaken candidate, reduces the keys across the
-// wave with DPP moves, and picks the holder of the maximum (the lowest chunk
-// index when several lanes hold it).  The winners are emitted in ascending
-// index order by a ballot and prefix popcount per slot; the window chunks
-// i-w..i follow them.
+// as an order-preserving 32-bit key of its score.  The k-1 winners are found
+// by a threshold search rather than k-1 arg-max rounds: a binary search over
+// the key bits, from the top, keeps the largest threshold T with at least
+// k-1 candidates >= T (each count a ballot and popcount per slot).  It stops
+// as soon as exactly k-1 candidates are >= T; otherwise T ends as the
+// (k-1)-th largest key, every candidate above T is kept and the remaining
+// places go to the candidates equal to T with the lowest chunk indices.
+// Either way the kept set is the first k-1 in the order score descending,
+// index ascending.  The winners are emitted in ascending index order by a
+// ballot and prefix popcount per slot; the window chunks i-w..i follow them.
 #pragma once
 
 #include "dhsa_internal.h"
@@ -38,43 +42,6 @@ __device__ __forceinline__ int64_t entries_before(int64_t i, int64_t k) {
   return i <= k ? i * (i + 1) / 2 : k * (k + 1) / 2 + (i - k) * k;
 }
 
-// Wave-wide max / min of a 32-bit value with DPP lane moves (no LDS round
-// trip): quad swaps, half-row and row mirrors, then row broadcasts carry the
-// result to lane 63, which is read back as a uniform value.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  uint32_t t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
-  v = v > t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
-  v = v > t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // row half mirror
-  v = v > t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);  // row mirror
-  v = v > t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row bcast 15
-  v = v > t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row bcast 31
-  v = v > t ? v : t;
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  uint32_t t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0xB1, 0xF, 0xF, false);
-  v = v < t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x4E, 0xF, 0xF, false);
-  v = v < t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x141, 0xF, 0xF, false);
-  v = v < t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x140, 0xF, 0xF, false);
-  v = v < t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xA, 0xF, false);
-  v = v < t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xC, 0xF, false);
-  v = v < t ? v : t;
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 // Writes the kept chunks of row i (ascending) to out[0 .. min(k+w, i+1)-1];
 // srow[j] is the score of key chunk j (j < i - w are read).  All 64 lanes
 // of the wave call it together; k >= 1, w >= 0.
@@ -92,29 +59,45 @@ __device__ __forceinline__ void select_row(const float* srow, int i, int k, int 
     const int j = lane + 64 * s;
     key[s] = j < older ? order_key(srow[j]) : 0u;  // 0: empty slot
   }
-  uint32_t taken = 0;
-  for (int round = 0; round < k - 1; ++round) {
-    // this lane's best untaken candidate (the lowest slot among equal keys)
-    uint32_t best = 0;
-    int bslot = 0;
+  // candidates with key >= y, across the wave (wave-uniform)
+  auto count_ge = [&](uint32_t y) {
+    int c = 0;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint32_t kv = ((taken >> s) & 1u) ? 0u : key[s];
-      if (kv > best) {
-        best = kv;
-        bslot = s;
+    for (int s = 0; s < NS; ++s) c += __popcll(__ballot(key[s] >= y));
+    return c;
+  };
+  const int need = k - 1;  // older >= k real candidates (keys >= 1) exist
+  uint32_t thr = 0;
+  int cthr = 64 * NS;      // count_ge(thr)
+  for (int bit = 31; bit >= 0 && need > 0; --bit) {
+    const uint32_t y = thr | (1u << bit);
+    const int c = count_ge(y);
+    if (c >= need) {
+      thr = y;
+      cthr = c;
+      if (c == need) break;
+    }
+  }
+  uint32_t taken = 0;
+  if (need > 0) {
+    if (cthr == need) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) taken |= (key[s] >= thr ? 1u : 0u) << s;
+    } else {
+      // thr is the need-th largest key: keep the keys above it, then the
+      // lowest-index keys equal to it (slot-major order is index order)
+      int rem = need - count_ge(thr + 1u);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bool eq = key[s] == thr;
+        const uint64_t m = __ballot(eq);
+        const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+        const bool sel = (key[s] > thr) || (eq && __popcll(below) < rem);
+        taken |= (sel ? 1u : 0u) << s;
+        const int pm = __popcll(m);
+        rem -= pm < rem ? pm : rem;
       }
     }
-    const uint32_t top = wave_max_u32(best);
-    const uint64_t holders = __ballot(best == top);
-    int wl;
-    if (__popcll(holders) == 1) {
-      wl = __ffsll((long long)holders) - 1;
-    } else {  // equal keys in several lanes: the lowest chunk index wins
-      const uint32_t j = best == top ? (uint32_t)(64 * bslot + lane) : 0xffffffffu;
-      wl = (int)(wave_min_u32(j) & 63u);
-    }
-    if (lane == wl) taken |= 1u << bslot;
   }
   // emit ascending: slot-major is index order
   int base = 0;
