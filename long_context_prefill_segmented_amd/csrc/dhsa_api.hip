@@ -152,28 +152,33 @@ int64_t query_tiles(int32_t batch, const int32_t* num_chunks, const int32_t* off
 
 // Query tile height for the attention kernel.  A 256-row tile (8 waves, one
 // workgroup per CU) streams each kept K/V sub-tile for twice as many rows as
-// a 128-row tile, but a chunk's last tile leaves waves idle; the large tile
-// is taken when at least 75 % of its 32-row wave slots hold query rows.
+// a 128-row tile, while a chunk of at most 128 rows leaves half of its waves
+// idle.  The large tile is taken when at least half of the tiled query rows
+// (remainders of at most kNarrowRows rows go to the narrow tiles either way)
+// lie in chunks longer than 128 rows.  Measured on 32K layers with uniform
+// chunk-length laws: U[33,128] and U[40,160] (0 % and 38 % of the rows in
+// longer chunks) run faster with 128-row tiles, U[64,192] (62 %), U[96,256],
+// U[128,384] and U[33,512] with 256-row tiles, as do the 16K, 32K, 128K and
+// ragged layers of the bench.
 // DHSA_ATTN_BLOCK_M=128|256 in the environment forces one of them.
 int32_t choose_block_m(int32_t batch, const int32_t* num_chunks, const int32_t* offs) {
   if (const char* env = getenv("DHSA_ATTN_BLOCK_M")) {
     const int v = atoi(env);
     if (v == kBlockMSmall || v == kBlockMLarge) return v;
   }
-  // remainders of at most kNarrowRows rows go to the narrow tiles either way
-  int64_t waves = 0, slots = 0;
+  int64_t rows = 0, long_rows = 0;
   size_t o = 0;
   for (int b = 0; b < batch; ++b) {
     for (int c = 0; c < num_chunks[b]; ++c) {
       const int64_t n = offs[o + c + 1] - offs[o + c];
       const int64_t full = n / kBlockMLarge, rem = n - full * kBlockMLarge;
       const int64_t wide_rows = rem <= kNarrowRows ? full * kBlockMLarge : n;
-      waves += (wide_rows + 31) / 32;
-      slots += (kBlockMLarge / 32) * ((wide_rows + kBlockMLarge - 1) / kBlockMLarge);
+      rows += wide_rows;
+      if (n > kBlockMSmall) long_rows += wide_rows;
     }
     o += num_chunks[b] + 1;
   }
-  return 4 * waves >= 3 * slots ? kBlockMLarge : kBlockMSmall;
+  return 2 * long_rows >= rows ? kBlockMLarge : kBlockMSmall;
 }
 
 int check_nms_sizes(int32_t batch, int32_t seq_len, int32_t min_gap) {
