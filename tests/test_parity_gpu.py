@@ -63,6 +63,9 @@ CASES = {
     # five sequences with different chunk counts and lengths
     "batch5": synth.small_workload("batch5", 5, 1536, 4, 2,
                                    ((0.6, 8, 64), (0.4, 100, 400)), "iid", topk=4, seed=44),
+    # DHSA_MAX_BATCH sequences: every per-sequence table entry in use
+    "max_batch": synth.small_workload("max_batch", 64, 256, 2, 1, (8, 64), "iid", topk=3,
+                                      seed=45),
 }
 
 _cache = {}
@@ -138,7 +141,7 @@ def assert_attention_close(gpu, ref, what):
 
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "unit_chunks",
-                                  "gqa16", "batch5"])
+                                  "gqa16", "batch5", "max_batch"])
 def test_pool_parity(name):
     c = get_case(name)
     for which, t, bits, H in (("q", c.q, c.x.q, c.hq), ("k", c.k, c.x.k, c.hkv)):
@@ -161,7 +164,7 @@ def test_pool_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "many_entries",
-                                  "many_chunks", "gqa16", "batch5"])
+                                  "many_chunks", "gqa16", "batch5", "max_batch"])
 def test_chunk_score_parity(name):
     c = get_case(name)
     say("  build_mask with scores")
@@ -183,7 +186,7 @@ def test_chunk_score_parity(name):
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "mha_dense",
                                   "topk1", "unit_chunks", "many_entries", "many_chunks",
-                                  "max_chunks", "gqa16", "batch5"])
+                                  "max_chunks", "gqa16", "batch5", "max_batch"])
 def test_topk_bit_exact_on_oracle_scores(name):
     c = get_case(name)
     flat = np.concatenate([r["s32"].reshape(-1) for r in c.ref]).astype(np.float32)
@@ -237,7 +240,7 @@ def test_topk_ties_and_signed_zero():
 
 
 @pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "topk1",
-                                  "many_chunks", "gqa16", "batch5"])
+                                  "many_chunks", "gqa16", "batch5", "max_batch"])
 def test_build_mask_matches_oracle_mask(name):
     c = get_case(name)
     csr = dhsa.build_mask(c.q, c.k, c.offs, c.topk)
@@ -293,7 +296,8 @@ def test_attention_on_oracle_mask(name, block_m):
     assert np.all(np.abs(lg - lse_ref) <= LSE_TOL * (1 + np.abs(lse_ref)))
 
 
-@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "gqa16", "batch5"])
+@pytest.mark.parametrize("name", ["tiny_1k", "mid_ragged", "mid_structured", "gqa16", "batch5",
+                                  "max_batch"])
 def test_attention_on_gpu_mask_end_to_end(name, block_m):
     c = get_case(name)
     csr = dhsa.build_mask(c.q, c.k, c.offs, c.topk)
