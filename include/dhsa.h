@@ -206,8 +206,9 @@ int dhsa_build_mask_ex(const void* q, const void* k,
  * workspace: device, >= dhsa_prefill_workspace_size bytes.
  * Limit: seq_len * num_kv_heads * 256 bytes (one sequence's K, or V) must
  * stay below 4 GiB (DHSA_ERR_UNSUPPORTED otherwise).
- * Query tiles are 256 rows when at least 75 % of their 32-row slots hold
- * rows, else 128; chunk remainders of at most 32 rows run in one-wave tiles.
+ * Query tiles are 256 rows when at least half of the tiled query rows lie in
+ * chunks longer than 128 rows, else 128; chunk remainders of at most 32 rows
+ * run in one-wave tiles.
  * The environment variable DHSA_ATTN_BLOCK_M=128 or 256 forces the height.
  * Results of the two heights agree to rounding: a row whose tile changes
  * between a wide kernel and the one-wave kernel sees 32-key instead of
