@@ -44,6 +44,9 @@ CASES = {
     # more than 4096 CSR rows: the budget scan runs over several blocks
     "scan_blocks": synth.small_workload("scan_blocks", 3, 4096, 4, 2, (2, 6), "iid", topk=5,
                                         seed=38),
+    # exactly DHSA_MAX_CHUNKS one-token chunks: the widest selection (32 slots per lane)
+    "max_chunks": synth.small_workload("max_chunks", 1, 2048, 2, 1, (1, 1), "iid", topk=9,
+                                       seed=39),
 }
 
 # (name of the budget rule, per-row budgets?, recent window, budget range)
