@@ -92,7 +92,6 @@ __global__ __launch_bounds__(kOrderThreads) void pool_order_kernel(
 // identity without one), then its column blocks of j0 followed by those of
 // j1, so every chunk's jobs sit together in the grid.
 __global__ __launch_bounds__(256) void pool_kernel(PoolJob j0, PoolJob j1,
-                                                   int32_t total_chunks,
                                                    const int32_t* __restrict__ offs,
                                                    SeqTable st, int32_t seq_len,
                                                    const int32_t* __restrict__ order) {
@@ -104,7 +103,6 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolJob j0, PoolJob j1,
   const PoolJob J = first ? j0 : j1;
   const int blk = first ? jb : jb - j0.nblk;
   const int cg = order ? order[rank] : rank;
-  (void)total_chunks;
   const int b = find_seq(st.cbase, st.batch, cg);
   const int c = cg - st.cbase[b];
   const int C = st.num_chunks[b];
@@ -189,8 +187,8 @@ hipError_t launch_pool(const uint16_t* x0, float* out0, int32_t h0,
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)grid), dim3(256), 0, stream, j0, j1,
-                     total_chunks, offs_dev, st, seq_len, static_cast<const int32_t*>(order));
+  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)grid), dim3(256), 0, stream, j0, j1, offs_dev,
+                     st, seq_len, static_cast<const int32_t*>(order));
   return hipGetLastError();
 }
 
