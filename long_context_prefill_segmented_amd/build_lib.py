@@ -24,6 +24,11 @@ LIB = os.path.join(PKG, "libdhsa.so")
 
 SOURCES = ["dhsa_api.hip", "pool.hip", "scores.hip", "topk.hip", "attn.hip", "nms.hip", "layer.hip"]
 
+# bench.py's streaming-read reference (a measuring aid, not part of libdhsa)
+BENCH_CSRC = os.path.join(PKG, "csrc_bench")
+BENCH_LIB = os.path.join(PKG, "libdhsa_bench.so")
+BENCH_SOURCES = ["hbm_read.hip"]
+
 COMMON_FLAGS = [
     "-x", "hip",
     "--offload-arch=gfx950",
@@ -61,14 +66,13 @@ def _run(cmd, what, verbose):
     return res
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libdhsa.so; returns the library path."""
+def _build_lib(srcdir, sources, lib, verbose):
     cc, hc = clang(), hipcc()
-    inc = ["-I", INCLUDE, "-I", CSRC]
+    inc = ["-I", INCLUDE, "-I", srcdir]
     with tempfile.TemporaryDirectory(prefix="dhsa_build_") as tmp:
         objs = []
-        for src in SOURCES:
-            path = os.path.join(CSRC, src)
+        for src in sources:
+            path = os.path.join(srcdir, src)
             fatbin = os.path.join(tmp, src.replace(".hip", ".fatbin"))
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             _run([cc, *COMMON_FLAGS, *DEVICE_FLAGS, *inc, "-c", path, "-o", fatbin],
@@ -76,11 +80,18 @@ def build(verbose: bool = False) -> str:
             _run([cc, *COMMON_FLAGS, *HOST_FLAGS, *inc, "-Xclang", "-fcuda-include-gpubinary",
                   "-Xclang", fatbin, "-c", path, "-o", obj], f"host pass of {src}", verbose)
             objs.append(obj)
-        tmp_lib = os.path.join(tmp, "libdhsa.so")
+        tmp_lib = os.path.join(tmp, os.path.basename(lib))
         _run([hc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib], "link",
              verbose)
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libdhsa.so (and bench.py's reference
+    library libdhsa_bench.so); returns the path of libdhsa.so."""
+    _build_lib(BENCH_CSRC, BENCH_SOURCES, BENCH_LIB, verbose)
+    return _build_lib(CSRC, SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":
