@@ -158,7 +158,7 @@ hipError_t launch_topk(const float* scores, const SeqTable& st, int32_t hq,
     return hipGetLastError();                                                               \
   }
   DHSA_TOPK_CASE(1) DHSA_TOPK_CASE(2) DHSA_TOPK_CASE(3) DHSA_TOPK_CASE(4)
-  DHSA_TOPK_CASE(5) DHSA_TOPK_CASE(6) DHSA_TOPK_CASE(8) DHSA_TOPK_CASE(10)
+  DHSA_TOPK_CASE(5) DHSA_TOPK_CASE(6) DHSA_TOPK_CASE(7) DHSA_TOPK_CASE(8) DHSA_TOPK_CASE(10)
   DHSA_TOPK_CASE(12) DHSA_TOPK_CASE(16) DHSA_TOPK_CASE(24) DHSA_TOPK_CASE(32)
 #undef DHSA_TOPK_CASE
   return hipErrorInvalidValue;
