@@ -336,8 +336,8 @@ int dhsa_pool(const void* x, int32_t batch, int32_t seq_len, int32_t num_heads, 
   SeqTable st;
   fill_table(st, batch, num_chunks, num_heads, 0);
   hipError_t e = launch_pool(static_cast<const uint16_t*>(x), pooled, num_heads, nullptr, nullptr, 0,
-                             (int32_t)total_chunks(batch, num_chunks), chunk_offsets_dev, st, seq_len,
-                             nullptr, static_cast<hipStream_t>(stream));
+                             (int32_t)total_chunks(batch, num_chunks), chunk_offsets_dev, nullptr,
+                             st, seq_len, nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   return ok();
 }
@@ -444,7 +444,7 @@ int dhsa_build_mask_ex(const void* q, const void* k, int32_t batch, int32_t seq_
   hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e = launch_pool(static_cast<const uint16_t*>(q), qbar, num_q_heads,
                              static_cast<const uint16_t*>(k), kbar, num_kv_heads, (int32_t)tc,
-                             chunk_offsets_dev, st, seq_len, order, strm);
+                             chunk_offsets_dev, chunk_offsets, st, seq_len, order, strm);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   e = launch_scores(qbar, kbar, scores, num_q_heads, num_kv_heads, st,
                     score_tiles(batch, num_chunks, num_q_heads), strm);

@@ -44,14 +44,17 @@ __device__ __forceinline__ int find_seq(const T* starts, int batch, T x) {
 
 // kernels' launchers (each returns hipGetLastError() of its launch)
 // order (nullable, total_chunks int32 of device scratch): the pooling grid
-// then runs the chunks longest first (a one-workgroup sort fills it), used
-// up to kPoolOrderMaxChunks chunks in all
+// then runs the chunks longest first, used up to kPoolOrderMaxChunks chunks
+// in all.  Up to kPoolOrderArgChunks chunks the host computes the order from
+// offs_host (the concatenated host offsets) and passes it in the kernel's
+// arguments; beyond that a one-workgroup device sort fills order.
 constexpr int kPoolOrderMaxChunks = 16384;
+constexpr int kPoolOrderArgChunks = 512;
 hipError_t launch_pool(const uint16_t* x0, float* out0, int32_t h0,
                        const uint16_t* x1, float* out1, int32_t h1,
                        int32_t total_chunks, const int32_t* offs_dev,
-                       const SeqTable& st, int32_t seq_len, int32_t* order,
-                       hipStream_t stream);
+                       const int32_t* offs_host, const SeqTable& st, int32_t seq_len,
+                       int32_t* order, hipStream_t stream);
 
 hipError_t launch_scores(const float* qbar, const float* kbar, float* scores,
                          int32_t hq, int32_t hkv, const SeqTable& st,

@@ -14,11 +14,13 @@
 //
 // Dispatch order: a workgroup's time grows with its chunk's length (64-512
 // tokens at 128K), so launching the chunks in index order leaves the longest
-// ones to the end of the grid.  A one-workgroup counting sort first lists the
-// chunks from the longest to the shortest (64 length buckets); the pooling
-// grid walks that list, which brings the makespan from 1.12-1.30x of an
-// even split down to about 1.02-1.05x (a list-scheduling simulation of the
-// 128K layer).  Results do not depend on the order.
+// ones to the end of the grid.  A counting sort lists the chunks from the
+// longest to the shortest (64 length buckets); the pooling grid walks that
+// list, which brings the makespan from 1.12-1.30x of an even split down to
+// about 1.02-1.05x (a list-scheduling simulation of the 128K layer).  Up to
+// 512 chunks the host sorts them and the list travels in the kernel's
+// arguments; above that a one-workgroup device kernel sorts them first.
+// Results do not depend on the order.
 #include "dhsa_internal.h"
 
 namespace dhsa {
@@ -34,6 +36,12 @@ struct PoolJob {
   float* out;
   int32_t heads;
   int32_t nblk;  // column blocks of kCols
+};
+
+// chunk order computed on the host (n == 0: none here)
+struct PoolOrderArg {
+  int32_t n;
+  uint16_t idx[kPoolOrderArgChunks];
 };
 
 __device__ __forceinline__ void add_bf16x8(float* acc, const u32x4& v) {
@@ -94,7 +102,8 @@ __global__ __launch_bounds__(kOrderThreads) void pool_order_kernel(
 __global__ __launch_bounds__(256) void pool_kernel(PoolJob j0, PoolJob j1,
                                                    const int32_t* __restrict__ offs,
                                                    SeqTable st, int32_t seq_len,
-                                                   const int32_t* __restrict__ order) {
+                                                   const int32_t* __restrict__ order,
+                                                   PoolOrderArg harg) {
   __shared__ float red[4][kCols];
   const int per_chunk = j0.nblk + j1.nblk;
   const int rank = (int)blockIdx.x / per_chunk;
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolJob j0, PoolJob j1,
   const bool first = jb < j0.nblk;
   const PoolJob J = first ? j0 : j1;
   const int blk = first ? jb : jb - j0.nblk;
-  const int cg = order ? order[rank] : rank;
+  const int cg = harg.n > 0 ? (int)harg.idx[rank] : (order ? order[rank] : rank);
   const int b = find_seq(st.cbase, st.batch, cg);
   const int c = cg - st.cbase[b];
   const int C = st.num_chunks[b];
@@ -173,14 +182,37 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolJob j0, PoolJob j1,
 hipError_t launch_pool(const uint16_t* x0, float* out0, int32_t h0,
                        const uint16_t* x1, float* out1, int32_t h1,
                        int32_t total_chunks, const int32_t* offs_dev,
-                       const SeqTable& st, int32_t seq_len, int32_t* order,
-                       hipStream_t stream) {
+                       const int32_t* offs_host, const SeqTable& st, int32_t seq_len,
+                       int32_t* order, hipStream_t stream) {
   PoolJob j0{x0, out0, h0, (h0 * kHeadDim + kCols - 1) / kCols};
   PoolJob j1{x1, out1, h1, x1 ? (h1 * kHeadDim + kCols - 1) / kCols : 0};
   const int64_t grid = (int64_t)total_chunks * (j0.nblk + j1.nblk);
   if (grid <= 0) return hipSuccess;
   // the sort pays for itself only while its strided passes are short
   if (order != nullptr && total_chunks > kPoolOrderMaxChunks) order = nullptr;
+  PoolOrderArg harg;
+  harg.n = 0;
+  if (order != nullptr && offs_host != nullptr && total_chunks <= kPoolOrderArgChunks) {
+    // the same bucket rule as pool_order_kernel, on the host
+    int len[kPoolOrderArgChunks];
+    int longest = 0;
+    int cg = 0;
+    for (int b = 0; b < st.batch; ++b) {
+      const int32_t* o = offs_host + st.cbase[b] + b;
+      for (int c = 0; c < st.num_chunks[b]; ++c, ++cg) {
+        len[cg] = o[c + 1] - o[c];
+        longest = len[cg] > longest ? len[cg] : longest;
+      }
+    }
+    const int64_t top = (int64_t)longest + 1;
+    int cnt[kOrderBuckets + 1] = {0};
+    auto bucket = [&](int n) { return kOrderBuckets - 1 - (int)((int64_t)n * kOrderBuckets / top); };
+    for (int c = 0; c < total_chunks; ++c) ++cnt[bucket(len[c]) + 1];
+    for (int u = 0; u < kOrderBuckets; ++u) cnt[u + 1] += cnt[u];
+    for (int c = 0; c < total_chunks; ++c) harg.idx[cnt[bucket(len[c])]++] = (uint16_t)c;
+    harg.n = total_chunks;
+    order = nullptr;
+  }
   if (order != nullptr) {
     hipLaunchKernelGGL(pool_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, offs_dev, st,
                        total_chunks, order);
@@ -188,7 +220,7 @@ hipError_t launch_pool(const uint16_t* x0, float* out0, int32_t h0,
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(pool_kernel, dim3((unsigned)grid), dim3(256), 0, stream, j0, j1, offs_dev,
-                     st, seq_len, static_cast<const int32_t*>(order));
+                     st, seq_len, static_cast<const int32_t*>(order), harg);
   return hipGetLastError();
 }
 
