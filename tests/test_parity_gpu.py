@@ -200,10 +200,11 @@ def test_topk_bit_exact_on_oracle_scores(name):
     np.testing.assert_array_equal(ci, c.ci)
 
 
-@pytest.mark.parametrize("name", ["mid_ragged", "mid_structured"])
+@pytest.mark.parametrize("name", ["mid_ragged", "mid_structured", "many_chunks", "max_batch"])
 def test_build_mask_equals_stage_kernels(name):
     # dhsa_build_mask and the stage calls (pool, chunk scores, top-k) run the
-    # same kernels: scores and masks must agree bit for bit
+    # same kernels: scores and masks must agree bit for bit, whichever way the
+    # pooling order is made (host sort up to 512 chunks, device sort above)
     c = get_case(name)
     csr, flat = dhsa.build_mask(c.q, c.k, c.offs, c.topk, return_scores=True)
     qbar = dhsa.pool(c.q, c.offs)
