@@ -92,7 +92,7 @@ __device__ __forceinline__ void select_row(const float* srow, int i, int k, int 
         const bool eq = key[s] == thr;
         const uint64_t m = __ballot(eq);
         const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
-        const bool sel = (key[s] > thr) || (eq && __popcll(below) < rem);
+        const bool sel = (key[s] > thr) || (eq && (int)__popcll(below) < rem);
         taken |= (sel ? 1u : 0u) << s;
         const int pm = __popcll(m);
         rem -= pm < rem ? pm : rem;

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / 64;
 
-__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v, int lane) {
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
   int32_t t;
   t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
   v += t;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kScanThreads) void budget_scan_kernel(
       }
     }
     const int32_t own = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-    const int32_t incl = wave_inclusive_scan(own, lane);
+    const int32_t incl = wave_inclusive_scan(own);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     int32_t before = carry;
